@@ -1,0 +1,134 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention library (libfa.so).
+ *
+ * Two operations, both asynchronous on the caller's HIP stream:
+ *
+ *   fa_fwd           fused, tiled attention forward O = softmax(scale * Q K^T) V with an
+ *                    online softmax; the N x N score and probability matrices never reach
+ *                    device memory.  Also writes the per-row log-sum-exp.
+ *   fa_paged_decode  one query token per sequence against a KV cache stored in fixed-size
+ *                    physical blocks that a block table addresses (non-contiguous gather).
+ *
+ * Conventions for every entry point
+ *   - Every data pointer is a caller-owned DEVICE pointer (e.g. from torch).  The library
+ *     allocates nothing, keeps no state between calls, never synchronises the host and never
+ *     prints.  It is safe to capture in a HIP graph.
+ *   - Results are valid once the caller has synchronised `stream` (a hipStream_t; NULL means
+ *     the default stream).
+ *   - Errors are reported through the return value only.  Argument validation happens before
+ *     any HIP call, so an invalid call has no side effect on the device.
+ *   - Values that live in device memory (sequence lengths, block ids) cannot be checked
+ *     without a synchronisation: sequence lengths are clamped to their valid range inside the
+ *     kernels; an out-of-range block id is undefined behaviour.
+ *   - All tensors are dense, row-major, with no padding between rows.  Data pointers must be
+ *     16-byte aligned.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, H % Hkv != 0,
+                             misaligned pointer, negative or non-finite scale,
+                             workspace too small, ... */
+  FA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dim not 64/128, unknown dtype,
+                             block size not 16, query-group size above 16, ... */
+  FA_ERR_HIP = 3          /* the HIP runtime reported an error (no device, launch failure) */
+} fa_status;
+
+/* Element type of q, k, v and o for fa_fwd. */
+enum { FA_BF16 = 0, /* bf16 storage, fp32 arithmetic and accumulation on the matrix cores */
+       FA_F32 = 1   /* fp32 storage and fp32 arithmetic throughout */ };
+
+/*
+ * fa_fwd -- attention forward.
+ *
+ * Computes, for every batch b and query head h (kv head g = h / (H / Hkv)):
+ *   S = scale * Q[b,h] K[b,g]^T,  P = softmax over each row of S,  O[b,h] = P V[b,g]
+ * as defined on the "GPU优化" tag page (guijiagi.com), excerpt "Flash Attention解决了什么问题？",
+ * algorithm part, with the scale passed explicitly (1/sqrt(d) for the standard layer).  The
+ * kernel follows the fused, tiled scheme of "Gemini 3 Flash的注意力内核重写：算子融合如何实现
+ * 亚毫秒级推理" (sections on kernel fusion, tiling and the online softmax) and the running
+ * statistics of "FlashAttention优化" §3.2.1: a running row maximum m and row sum l, rescaled
+ * whenever m grows, the output normalised once at the end.
+ *
+ *   q         [B, H, N, d]    element type `dtype`
+ *   k, v      [B, Hkv, N, d]  element type `dtype`
+ *   o         [B, H, N, d]    element type `dtype`, written
+ *   lse       [B, H, N] fp32, written: natural-log log-sum-exp of the scaled scores of each
+ *             row, max_j(S_ij) + ln(sum_j exp(S_ij - max_j S_ij)) -- the per-row statistic a
+ *             recompute backward needs (page "Gemini 3 Flash的注意力内核重写", §4 on
+ *             recomputation keeps each row's maximum and normaliser).
+ *   B, H, Hkv, N  > 0, H % Hkv == 0 (grouped-query heads share kv heads in consecutive groups;
+ *             "FlashAttention优化" §5.3).
+ *   d         head dimension: 64 or 128.
+ *   scale     finite and >= 0.
+ *   causal    nonzero: key j is visible to query i only if j <= i (square, diagonal kept).
+ *   seq_lens  NULL, or a device int32[B] of valid lengths L_b (clamped to [0, N]): keys
+ *             j >= L_b are masked and query rows i >= L_b are padding, written as O = 0 and
+ *             lse = -inf.  Combines with `causal`.
+ *   dtype     FA_BF16 or FA_F32.
+ *   stream    hipStream_t or NULL.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, float scale, int causal, const int32_t* seq_lens,
+                 int dtype, void* stream);
+
+/*
+ * fa_paged_decode_workspace_bytes -- size in bytes of the device workspace fa_paged_decode
+ * needs for these sizes (partial outputs and statistics of the key-range splits).  Returns 0
+ * for non-positive sizes.
+ */
+size_t fa_paged_decode_workspace_bytes(int num_seqs, int Hq, int d, int max_blocks_per_seq,
+                                       int block_size);
+
+/*
+ * fa_paged_decode -- decode attention over a paged KV cache.
+ *
+ * One query token per sequence attends to all L_b cached tokens of its sequence.  The cache
+ * is stored in physical blocks of `block_size` tokens scattered through a pool; token t of
+ * sequence b lives in block block_table[b][t / block_size] at slot t % block_size.  The kernel
+ * prefetches the block ids into registers, gathers each block's keys and values with
+ * coalesced loads through on-chip memory and attends to them in the same kernel, following
+ * the non-contiguous block gather page (ocdem.com, vLLM PagedAttention rework) §二.1 (two-stage
+ * gather through shared memory), §二.3 (index prefetch into registers) and §二.4 (gather and
+ * attention fused).  Long sequences are cut into key ranges processed in parallel whose
+ * partial (max, sum, output) triples are merged exactly, as the online-softmax recurrence of
+ * "FlashAttention优化" §3.2 allows for any block order.
+ *
+ *   q            [num_seqs, Hq, d] bf16
+ *   k_cache      [num_blocks, block_size, Hkv, d] bf16
+ *   v_cache      [num_blocks, block_size, Hkv, d] bf16
+ *   block_table  [num_seqs, max_blocks_per_seq] int32 physical block ids in [0, num_blocks);
+ *                entries at index >= ceil(L_b / block_size) are never read.
+ *   seq_lens     [num_seqs] int32 (device), clamped to [0, max_blocks_per_seq * block_size].
+ *                A sequence of length 0 gives O = 0 and lse = -inf.
+ *   o            [num_seqs, Hq, d] bf16, written.
+ *   lse          [num_seqs, Hq] fp32, written (natural log, as for fa_fwd), or NULL.
+ *   Hq % Hkv == 0 and Hq / Hkv <= 16.  d: 64 or 128.  block_size: 16.
+ *   scale        finite and >= 0.
+ *   workspace    device buffer of at least fa_paged_decode_workspace_bytes(...) bytes,
+ *                16-byte aligned, owned by the caller; its contents on entry do not matter.
+ *   stream       hipStream_t or NULL.  Calls that share a workspace must be ordered.
+ */
+fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* o,
+                          float* lse, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* fa_status_str -- static, NUL-terminated description of a status code. */
+const char* fa_status_str(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs shared by the kernels' tests, the bench and the oracle checks.
+
+This module only draws random numbers and lays them out; it holds none of attention's
+arithmetic, so both the HIP path and the CPU oracle can consume its output without sharing
+code.  Every tensor is drawn on the CPU from a ``torch.Generator`` seeded explicitly, so a
+given (shape, seed) always yields the same bytes on any host.
+
+Recipe (the workload list that the measurements quote):
+* prefill: q, k, v drawn in that order as float32 N(0, 1), then rounded to the storage dtype
+  (bf16 round-to-nearest-even, or kept float32); layout [B, H, N, d] / [B, Hkv, N, d].
+  With per-sequence lengths, ``seq_lens`` is drawn after v, uniform in [lo, hi].
+* paged decode: ``seq_lens`` uniform in [lo, hi] first, then a random permutation that places
+  each sequence's logical blocks in the pool, then q [S, Hq, d], then the K pool and the V pool
+  [num_blocks, block_size, Hkv, d], all N(0, 1) rounded to bf16.  Unused block-table entries
+  are -1.  The pool holds exactly sum(ceil(L_b / block_size)) blocks, so every cached byte is
+  distinct and comes from HBM once per decode step.
+"""
+
+import math
+
+import torch
+
+__all__ = [
+    "prefill_inputs",
+    "varlen_lengths",
+    "paged_decode_inputs",
+    "WORKLOADS",
+]
+
+# The five workloads the measurements and parity cases are quoted on.
+WORKLOADS = {
+    "single_head_fp32": dict(B=1, H=1, Hkv=1, N=256, d=64, dtype="f32", causal=False, seed=1),
+    "prefill_4k": dict(B=1, H=8, Hkv=8, N=4096, d=128, dtype="bf16", causal=False, seed=2),
+    "prefill_16k": dict(B=1, H=8, Hkv=8, N=16384, d=128, dtype="bf16", causal=False, seed=3),
+    "prefill_16k_causal": dict(B=1, H=8, Hkv=8, N=16384, d=128, dtype="bf16", causal=True, seed=3),
+    "gqa_varlen_8k": dict(B=4, H=32, Hkv=8, N=8192, d=128, dtype="bf16", causal=True, seed=4,
+                          len_lo=2048, len_hi=8192),
+    "paged_decode": dict(S=64, Hq=32, Hkv=8, d=128, block_size=16, len_lo=512, len_hi=32768,
+                         seed=5),
+}
+
+_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _gen(seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, gen, dtype, chunk=1 << 26):
+    """N(0,1) float32 draws rounded to ``dtype``; drawn in chunks to bound host memory."""
+    out = torch.empty(shape, dtype=dtype)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        flat[s:e] = torch.randn(e - s, generator=gen, dtype=torch.float32).to(dtype)
+    return out
+
+
+def prefill_inputs(B, H, Hkv, N, d, dtype="bf16", seed=0, len_lo=None, len_hi=None):
+    """(q, k, v, seq_lens) on the CPU.  seq_lens is None unless len_lo/len_hi are given."""
+    dt = _DTYPES[dtype]
+    g = _gen(seed)
+    q = _randn((B, H, N, d), g, dt)
+    k = _randn((B, Hkv, N, d), g, dt)
+    v = _randn((B, Hkv, N, d), g, dt)
+    seq_lens = None
+    if len_lo is not None:
+        seq_lens = varlen_lengths(B, len_lo, len_hi, g)
+    return q, k, v, seq_lens
+
+
+def varlen_lengths(B, lo, hi, gen):
+    """B int32 lengths uniform in [lo, hi]."""
+    return torch.randint(int(lo), int(hi) + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+
+
+def paged_decode_inputs(S, Hq, Hkv, d, block_size=16, len_lo=512, len_hi=32768, seed=0,
+                        seq_lens=None, spare_blocks=0):
+    """(q, k_cache, v_cache, block_table, seq_lens) on the CPU, bf16 data, int32 indices.
+
+    ``seq_lens`` may be given explicitly (a list); otherwise it is drawn.  ``spare_blocks``
+    adds unreferenced blocks to the pool (their ids are shuffled in with the used ones).
+    """
+    g = _gen(seed)
+    if seq_lens is None:
+        lens = torch.randint(int(len_lo), int(len_hi) + 1, (S,), generator=g, dtype=torch.int64)
+    else:
+        lens = torch.as_tensor(list(seq_lens), dtype=torch.int64)
+        if lens.numel() != S:
+            raise ValueError("seq_lens must have S entries")
+    nblk = [int(math.ceil(int(x) / block_size)) for x in lens]
+    max_blocks = max(1, max(nblk))
+    used = sum(nblk)
+    pool = used + int(spare_blocks)
+    perm = torch.randperm(max(pool, 1), generator=g, dtype=torch.int64)[:pool]
+    table = torch.full((S, max_blocks), -1, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+    q = _randn((S, Hq, d), g, torch.bfloat16)
+    k_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
+    v_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
+    return q, k_cache, v_cache, table, lens.to(torch.int32)

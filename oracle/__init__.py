@@ -1,0 +1,23 @@
+"""CPU oracle for fused attention forward and paged decode -- TEST INFRASTRUCTURE.
+
+This package is the slow, obviously-correct fp64 reference that the HIP kernels are
+checked against.  Only the test-suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  The product path (the C-ABI library
+and its Python binding) never imports, calls or links anything here, and this package
+imports nothing from the product: the two share no code.
+
+What it computes is the plain definition of attention written out (no tiling, no
+fusion, no online softmax):
+
+* ``attention_ref``     -- materialised three-pass softmax attention (prefill).
+* ``paged_decode_ref``  -- one query row per sequence against a KV cache stored in
+                           fixed-size physical blocks addressed through a block table.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against closed forms,
+invariances, a pure-Python brute force and a library routine.
+"""
+
+from .attention import attention_ref, attention_probs_ref
+from .paged import paged_decode_ref, gather_paged_kv
+
+__all__ = ["attention_ref", "attention_probs_ref", "paged_decode_ref", "gather_paged_kv"]

@@ -1,0 +1,66 @@
+"""Paged decode attention in float64 (oracle; test infrastructure).
+
+Page "非连续块Gather" (ocdem.com, vLLM PagedAttention kernel rework) §二.1 and §二.3: the keys
+and values of one sequence live in physical blocks scattered through a pool, found through an
+index array.  This oracle gathers them back into a contiguous sequence, token by token, and
+then applies the same three-pass softmax attention as ``attention.py`` with a single query row
+that sees every cached token (the query is the newest token; "FlashAttention优化" §4.2.2
+describes decode as one token against the O(N d) cache).
+
+Layouts (readings listed in the design doc):
+* q        [S, Hq, d]
+* k_cache  [num_blocks, block_size, Hkv, d]   (token-major inside a block)
+* v_cache  same as k_cache
+* block_table [S, max_blocks] integer physical block ids; entry t // block_size holds token t
+* seq_lens [S]; a sequence of length 0 yields O = 0, LSE = -inf.
+Query head h reads kv head h // (Hq // Hkv).
+"""
+
+import numpy as np
+
+__all__ = ["gather_paged_kv", "paged_decode_ref"]
+
+
+def gather_paged_kv(cache, block_table_row, length):
+    """Contiguous [length, Hkv, d] float64 view of one sequence's tokens from a paged pool.
+
+    Token t lives in physical block block_table_row[t // block_size] at slot t % block_size.
+    """
+    cache = np.asarray(cache)
+    bs = cache.shape[1]
+    t = np.arange(length)
+    blocks = np.asarray(block_table_row, dtype=np.int64)[t // bs]
+    if length and (blocks.min() < 0 or blocks.max() >= cache.shape[0]):
+        raise ValueError("block id out of range")
+    return cache[blocks, t % bs].astype(np.float64)
+
+
+def paged_decode_ref(q, k_cache, v_cache, block_table, seq_lens, scale):
+    """One decode step: O [S, Hq, d] and LSE [S, Hq] in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    S, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d or Hq % Hkv != 0:
+        raise ValueError("inconsistent shapes")
+    group = Hq // Hkv
+    lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
+    o = np.zeros((S, Hq, d))
+    lse = np.full((S, Hq), -np.inf)
+    for b in range(S):
+        L = lens[b]
+        if L == 0:
+            continue
+        kb = gather_paged_kv(k_cache, block_table[b], L)    # [L, Hkv, d]
+        vb = gather_paged_kv(v_cache, block_table[b], L)
+        for h in range(Hq):
+            g = h // group
+            # pass 1: scores of the single query row and their maximum
+            s = float(scale) * (kb[:, g, :] @ q[b, h])
+            m = s.max()
+            # pass 2: exponentials and their sum
+            e = np.exp(s - m)
+            l = e.sum()
+            # pass 3: normalise and weight the values
+            o[b, h] = (e / l) @ vb[:, g, :]
+            lse[b, h] = m + np.log(l)
+    return o, lse
