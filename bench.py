@@ -1,0 +1,244 @@
+"""Throughput of the fused attention forward and the paged decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+
+One step is one pass of the whole hot path over its synthetic batch:
+  * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
+  * fa_paged_decode on 64 sequences x 1 query token, Hq=32 Hkv=8 d=128 bf16, 16-token blocks
+    shuffled through a pool, lengths uniform in [512, 32768].
+W untimed steps, then K timed steps between device synchronisations.  Each call is also
+bracketed by HIP events on the stream it is launched on, so every kernel's own average
+duration is known.  ``value`` is the forward's TFLOP/s (4*B*H*N^2*d / average forward time);
+the decode's GB/s (algorithmic bytes / average decode time) is reported beside it.  Inputs are
+resident in device memory before the timed region starts.
+
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (% MFMA peak) at N=16384,d=128; decode GB/s (% HBM)"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _time_calls(torch, fn, iters):
+    """Average ms of fn() over iters calls, HIP events on the current stream."""
+    evs = [_events(torch) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / iters
+
+
+def cpu_baseline(prefill_inputs, w, budget_s=10.0):
+    """The fp64 oracle on a bounded sample of the forward workload: the first R query rows of
+    successive heads against all N keys, until about budget_s seconds of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_ref
+
+    q, k, v, _ = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], "bf16", seed=w["seed"])
+    qf = q.float().numpy().astype(np.float64)
+    kf = k.float().numpy().astype(np.float64)
+    vf = v.float().numpy().astype(np.float64)
+    R = 2048
+    rows = list(range(R))
+    N, d = w["N"], w["d"]
+    done, elapsed = 0, 0.0
+    for h in range(w["H"]):
+        t0 = time.perf_counter()
+        attention_ref(qf[:, h:h + 1], kf[:, h:h + 1], vf[:, h:h + 1], 1 / math.sqrt(d), rows=rows)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    flops = 4.0 * done * R * N * d
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 three-pass oracle, first {R} query rows of {done} head(s) x {N} keys, "
+                  f"d={d} ({elapsed:.1f} s); same flop formula as the GPU figure",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "prefill shards by heads and decode by sequences with no exchange, so the "
+              "per-GPU kernel at its share is what one GPU shows.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_attention_02_amd import fa_fwd, fa_paged_decode, fa_paged_decode_workspace_bytes
+    from io_aware_attention_02_amd import accounting as acc
+    from io_aware_attention_02_amd.inputs import WORKLOADS, paged_decode_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    wf = WORKLOADS["prefill_16k"]
+    wd = WORKLOADS["paged_decode"]
+
+    q, k, v, _ = prefill_inputs(wf["B"], wf["H"], wf["Hkv"], wf["N"], wf["d"], "bf16", seed=wf["seed"])
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wf["B"], wf["H"], wf["N"]), dtype=torch.float32, device=dev)
+
+    dq, kc, vc, table, lens = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
+                                                  wd["block_size"], wd["len_lo"], wd["len_hi"],
+                                                  seed=wd["seed"])
+    lens_host = lens.tolist()
+    dq, kc, vc, table, lens = dq.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev)
+    do = torch.empty_like(dq)
+    dlse = torch.empty((wd["S"], wd["Hq"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, fa_paged_decode_workspace_bytes(wd["S"], wd["Hq"], wd["d"],
+                                                             table.shape[1], wd["block_size"])),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        fa_fwd(q, k, v, o, lse, causal=False)
+
+    def decode():
+        fa_paged_decode(dq, kc, vc, table, lens, do, dlse, workspace=ws)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(_events(torch), _events(torch)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for (pa, pb), (da, db) in ev:
+        pa.record()
+        prefill()
+        pb.record()
+        da.record()
+        decode()
+        db.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = sum(a.elapsed_time(b) for (a, b), _ in ev) / K      # ms
+    t_dec = sum(a.elapsed_time(b) for _, (a, b) in ev) / K      # ms
+
+    flops = acc.attention_flops(wf["B"], wf["H"], wf["N"], wf["d"], causal=False)
+    tflops = flops / (t_pre * 1e-3) / 1e12
+    dbytes = acc.decode_bytes(lens_host, wd["Hq"], wd["Hkv"], wd["d"], wd["block_size"])
+    gbps = dbytes / (t_dec * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+        traffic = tr.get("fwd_bf16_kernel", {}).get("hbm_bytes_per_launch")
+        dec_traffic = tr.get("decode_split_kernel", {}).get("hbm_bytes_per_launch")
+    else:
+        dec_traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fa_fwd B=1 H=8 N=16384 d=128 bf16 non-causal; then fa_paged_decode "
+                        "64 seqs x 1 token, Hq=32 Hkv=8 d=128 bf16, 16-token blocks, "
+                        "lengths U[512,32768]",
+            "global_batch": wf["B"],
+            "seq_len": wf["N"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": acc.MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / acc.MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "fwd_bf16_kernel",
+            "ms_per_launch": round(t_pre, 4),
+            "flops_per_launch": flops,
+        },
+        "decode": {
+            "value": round(gbps, 1),
+            "unit": "GB/s",
+            "ms_per_call": round(t_dec, 4),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(gbps, 1),
+                "peak": acc.MI355X_HBM_GBPS,
+                "unit": "GB/s",
+                "frac": round(gbps / acc.MI355X_HBM_GBPS, 4),
+                "traffic": dec_traffic,
+                "bytes_per_call": dbytes,
+            },
+        },
+    }
+
+    if not args.no_extras:
+        extras = {}
+        wc = WORKLOADS["prefill_16k_causal"]
+        t = _time_calls(torch, lambda: fa_fwd(q, k, v, o, lse, causal=True), 10)
+        f = acc.attention_flops(wc["B"], wc["H"], wc["N"], wc["d"], causal=True)
+        extras["prefill_16k_causal"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2)}
+        w2 = WORKLOADS["prefill_4k"]
+        q2, k2, v2, _ = prefill_inputs(w2["B"], w2["H"], w2["Hkv"], w2["N"], w2["d"], "bf16", seed=w2["seed"])
+        q2, k2, v2 = q2.to(dev), k2.to(dev), v2.to(dev)
+        t = _time_calls(torch, lambda: fa_fwd(q2, k2, v2, causal=False), 20)
+        f = acc.attention_flops(w2["B"], w2["H"], w2["N"], w2["d"])
+        extras["prefill_4k"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2)}
+        w4 = WORKLOADS["gqa_varlen_8k"]
+        q4, k4, v4, l4 = prefill_inputs(w4["B"], w4["H"], w4["Hkv"], w4["N"], w4["d"], "bf16",
+                                        seed=w4["seed"], len_lo=w4["len_lo"], len_hi=w4["len_hi"])
+        lh = l4.tolist()
+        q4, k4, v4, l4 = q4.to(dev), k4.to(dev), v4.to(dev), l4.to(dev)
+        t = _time_calls(torch, lambda: fa_fwd(q4, k4, v4, causal=True, seq_lens=l4), 10)
+        f = acc.attention_flops(w4["B"], w4["H"], w4["N"], w4["d"], causal=True, seq_lens=lh)
+        extras["gqa_varlen_8k_causal"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
+                                          "seq_lens": lh}
+        out["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(prefill_inputs, wf)
+    else:
+        out["cpu_baseline"] = None
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+// fa_api.cpp -- the C ABI of libfa.so (declared in include/fa.h).
+//
+// Every entry point validates its arguments completely before touching the HIP runtime, so
+// a rejected call has no device-side effect, then launches the kernels on the caller's
+// stream and reports the launch status.  Nothing here allocates, synchronises or prints.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_scale(float s) { return std::isfinite(s) && s >= 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status status) {
+  switch (status) {
+    case FA_OK:
+      return "ok";
+    case FA_ERR_INVALID_ARG:
+      return "invalid argument";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case FA_ERR_HIP:
+      return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, float scale, int causal, const int32_t* seq_lens,
+                 int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // One workgroup per (batch, head, query tile of >= 32 rows) must fit a 1-D grid.
+  const long long tiles = (long long)B * H * ((N + 31) / 32);
+  if (tiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_paged_decode_workspace_bytes(int num_seqs, int Hq, int d, int max_blocks_per_seq,
+                                       int block_size) {
+  return fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);
+}
+
+fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* o,
+                          float* lse, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (block_size != 16) return FA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  // Grid: (Hkv, key-range splits, sequences); the last two dimensions are limited to 65535.
+  const long long splits =
+      ((long long)max_blocks_per_seq * block_size + fa::kDecodeSplitTokens - 1) /
+      fa::kDecodeSplitTokens;
+  if (splits > 65535 || num_seqs > 65535) return FA_ERR_UNSUPPORTED;
+  const size_t need =
+      fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.S = num_seqs;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.block_size = block_size;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  a.workspace = workspace;
+  const hipError_t e = fa::launch_paged_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

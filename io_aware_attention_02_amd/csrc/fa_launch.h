@@ -1,0 +1,44 @@
+// fa_launch.h -- internal interface between the C-ABI layer (fa_api.cpp) and the kernels.
+// Arguments are already validated when these run; each returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seq_lens;  // nullptr: every sequence has N valid rows
+  int B, H, Hkv, N, d;
+  float scale;
+  bool causal;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;  // may be nullptr
+  int S, Hq, Hkv, d, block_size, max_blocks, num_blocks;
+  float scale;
+  void* workspace;
+};
+
+// Tokens per key-range split of the decode kernel and the resulting workspace size.
+constexpr int kDecodeSplitTokens = 512;
+size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size);
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa
