@@ -1,6 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+    python bench.py --only {fwd,fwd_causal,decode,copy} [--steps K]   (one kernel, for profilers)
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -83,6 +84,42 @@ def cpu_baseline(prefill_inputs, w, budget_s=10.0):
     }
 
 
+def only(args, torch, dev, wf, wd):
+    """One kernel alone, W untimed + K timed calls: the command the profiles are taken with."""
+    from io_aware_attention_02_amd import fa_fwd, fa_paged_decode
+    from io_aware_attention_02_amd.inputs import paged_decode_inputs, prefill_inputs
+
+    if args.only in ("fwd", "fwd_causal"):
+        q, k, v, _ = prefill_inputs(wf["B"], wf["H"], wf["Hkv"], wf["N"], wf["d"], "bf16",
+                                    seed=wf["seed"])
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((wf["B"], wf["H"], wf["N"]), dtype=torch.float32, device=dev)
+        causal = args.only == "fwd_causal"
+        fn = lambda: fa_fwd(q, k, v, o, lse, causal=causal)  # noqa: E731
+        what = f"fa_fwd B=1 H=8 N=16384 d=128 bf16 causal={causal}"
+    elif args.only == "decode":
+        dq, kc, vc, table, lens = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
+                                                      wd["block_size"], wd["len_lo"], wd["len_hi"],
+                                                      seed=wd["seed"])
+        dq, kc, vc, table, lens = dq.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev)
+        do = torch.empty_like(dq)
+        fn = lambda: fa_paged_decode(dq, kc, vc, table, lens, do)  # noqa: E731
+        what = "fa_paged_decode 64 seqs Hq=32 Hkv=8 d=128 lens U[512,32768]"
+    else:
+        n = 1 << 29  # 512 Mi bf16 elements: 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)  # noqa: E731
+        what = "device copy of 1 GiB (bf16), the byte-counter calibration"
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    ms = _time_calls(torch, fn, args.steps)
+    print(json.dumps({"only": args.only, "what": what, "calls": args.steps, "ms_per_call": round(ms, 4)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "fwd_causal", "decode", "copy"], default=None,
+                    help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -106,6 +145,9 @@ def main():
     dev = torch.device("cuda:0")
     wf = WORKLOADS["prefill_16k"]
     wd = WORKLOADS["paged_decode"]
+    if args.only is not None:
+        only(args, torch, dev, wf, wd)
+        return
 
     q, k, v, _ = prefill_inputs(wf["B"], wf["H"], wf["Hkv"], wf["N"], wf["d"], "bf16", seed=wf["seed"])
     q, k, v = q.to(dev), k.to(dev), v.to(dev)

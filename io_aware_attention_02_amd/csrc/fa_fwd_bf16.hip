@@ -2,57 +2,83 @@
 //
 // One workgroup owns BM query rows of one (batch, head) and streams that head's K/V in tiles
 // of BN keys through LDS (the fused, tiled scheme of "Gemini 3 Flash的注意力内核重写" -- kernel
-// fusion, tiling -- and "FlashAttention优化" §3.1, with the query block resident and all K/V
-// blocks streamed past it).  Per tile it computes scores on the matrix cores, updates the
+// fusion, tiling -- and "FlashAttention优化" §3.1: the query block stays resident and every
+// K/V block streams past it).  Per tile it computes scores on the matrix cores, updates the
 // running row maximum and row sum with the online-softmax recurrence of "FlashAttention优化"
-// §3.2.1, rescales the output accumulator and adds P V on the matrix cores.  Scores and
-// probabilities live only in registers.  The output is divided by the row sum once at the
-// end (the deferred rescale the "GPU优化" tag page attributes to FlashAttention V2), and the
-// natural-log LSE of each row is written beside it.
+// §3.2.1, and adds P V on the matrix cores.  Scores and probabilities live only in registers.
+// The output is divided by the row sum once at the end (the deferred rescale the "GPU优化" tag
+// page attributes to FlashAttention V2) and the natural-log LSE of each row is written beside
+// it.
 //
-// CDNA4 mapping (not the pages' A100/H100 tile sizes):
-//  * Each wave owns 32*QB query rows.  Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: K rows (keys) are the A operand read from LDS, Q^T is the B
-//    operand held in registers for the whole kernel.  The accumulator then holds one query per
-//    lane (lane & 31) and 16 keys per lane, so row max / row sum are mostly in-lane and need
-//    one exchange with lane ^ 32 (v_permlane32_swap).  The row sum is kept per half-wave and
-//    combined once in the epilogue.
-//  * The probabilities of a lane are already the B operand of O^T += V^T P^T (keys in
-//    k-slots, query in the lane) after packing to bf16, so P never leaves registers.  V is
-//    written to LDS transposed ([dim][key]) with the key order permuted to match the k-slot
-//    order of the score accumulator; both contractions then read 16 contiguous bytes per lane.
-//  * K/V tiles are double-buffered in LDS: the global loads of tile j+2 are in flight while
-//    tile j is computed; tile j+1 goes from registers to the other buffer after it.  One
-//    barrier per tile.  LDS rows are padded by 16 bytes so that 16-byte reads of consecutive
-//    rows fall in distinct banks.
+// CDNA4 mapping (the pages' A100/H100 tile sizes are prior art, not used):
+//  * 4 waves x 32 query rows (BM = 128), BN = 64 keys per tile.  A wave holds its Q^T
+//    fragments, two score tiles and the 32 x d output accumulator in registers (<= 256 per
+//    lane), so two workgroups share a CU and the two waves on every SIMD come from different
+//    workgroups: one's softmax (VALU) overlaps the other's matrix work.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows are
+//    the A operand (read from LDS), Q^T the B operand (registers).  The accumulator holds one
+//    query per lane and 16 keys per lane, so the row max/sum are in-lane plus one exchange with
+//    lane ^ 32 (v_permlane32_swap).  Packed to bf16, a lane's probabilities are already the B
+//    operand of O^T += V^T P^T (keys in k-slots), so P never leaves registers.
+//  * K and V go from global memory straight into LDS (global_load_lds_dwordx4, no staging
+//    registers), into two buffers each.  The 16-byte chunks of a row are XOR-swizzled by row
+//    so that the fragment reads are free of bank conflicts.  V stays [key][dim] in LDS; its
+//    V^T fragments are read with ds_read_b64_tr_b16, the gfx950 transposing LDS read (each
+//    16-lane group turns a 4-key x 16-dim block into 4 consecutive keys per lane).
+//  * Software pipeline inside a wave: while the matrix cores compute S_{j+1} = Q K_{j+1}^T,
+//    the VALU turns S_j into probabilities; while they compute O += V_j P_j, the VALU takes
+//    the row maxima of S_{j+1}.  The loads of K_{j+2} and V_{j+1} are in flight meanwhile.
+//    One barrier per tile.
+//  * Lazy rescaling: the reference maximum m used in exp2(s - m) only moves when a row's
+//    maximum exceeds it by more than 2^8 (a wave-uniform test).  Probabilities are then at most
+//    256, and since the output and the row sum share the same reference, O = acc / l and
+//    LSE = m + log l are unchanged -- this is the rescale rule of §3.2.1 applied only when it
+//    is needed, not an approximation.
 //  * The grid is one workgroup per (batch, head, query tile), remapped so that the tiles of one
 //    head (and of one grouped-query kv head) run on the same XCD and share its L2.  Under
 //    causal masking the heaviest query tiles are issued first, tiles past the diagonal are
-//    never loaded, and waves whose rows are all above a tile skip it.
+//    never loaded, and a wave whose rows all lie above a tile skips its arithmetic.
 #include "fa_device.h"
 #include "fa_launch.h"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
 
-template <int D, int QB, int NW>
-struct Tile {
-  static constexpr int BN = 64;             // keys per K/V tile
-  static constexpr int WQ = 32 * QB;        // query rows per wave
-  static constexpr int BM = WQ * NW;        // query rows per workgroup
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int KS = D + 8;          // LDS row stride of the K tile (elements)
-  static constexpr int VS = BN + 8;         // LDS row stride of the transposed V tile
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr int DC = D / 8;          // 16-byte chunks per row
-  static constexpr int K_CHUNKS = BN * DC;
-  static constexpr int K_ITERS = (K_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int V_UNITS = (BN / 4) * DC;  // 4 keys x 8 dims per unit
-  static constexpr int V_ITERS = (V_UNITS + THREADS - 1) / THREADS;
-  static constexpr int NB = D / 32;         // 32-dim blocks of the output
-  static constexpr int KC = D / 16;         // 16-dim chunks of the score contraction
+typedef __attribute__((address_space(3))) char lds_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+constexpr int kNW = 4;                 // waves per workgroup
+constexpr int kWQ = 32;                // query rows per wave
+constexpr int kBM = kNW * kWQ;         // query rows per workgroup
+constexpr int kBN = 64;                // keys per tile
+constexpr int kThreads = 64 * kNW;
+constexpr float kTau = 8.f;            // lazy-rescale threshold (log2 units)
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
+#ifndef FA_FWD_PIPE
+#define FA_FWD_PIPE 0
+#endif
+constexpr bool kPipe = FA_FWD_PIPE;    // software-pipelined variant (see the loop below)
+
+template <int D>
+struct Geo {
+  static constexpr int RB = D * 2;                 // bytes per K/V row
+  static constexpr int CPR = RB / 16;              // 16-byte chunks per row
+  static constexpr int TILE = kBN * RB;            // bytes per K or V tile
+  static constexpr int NI = TILE / 1024;           // 1 KB direct loads per tile
+  static constexpr int NI_W = NI / kNW;            // ... per wave
+  static constexpr int RPI = 1024 / RB;            // rows per direct load
+  static constexpr int KC = D / 16;                // 16-dim steps of the score contraction
+  static constexpr int NB = D / 32;                // 32-dim blocks of the output
+  static_assert(NI % kNW == 0, "tile loads split evenly over the waves");
+  // Chunk swizzles (XOR on the 16-byte chunk index of a row).  K: 16 consecutive rows read at
+  // one logical chunk hit 16 distinct bank groups.  V: the 8 rows x 64 bytes that one
+  // transposing read touches cover every bank group exactly twice.
+  __device__ static int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ static int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
 struct Params {
@@ -66,86 +92,192 @@ struct Params {
   float sl2;  // scale * log2(e): scores go to the exponent base 2
 };
 
-template <class T>
-struct Stage {
-  u32x4 k[T::K_ITERS];
-  u32x4 v[T::V_ITERS][4];
+// Per-lane byte offsets of this wave's direct loads inside a tile (row * RB + swizzled chunk).
+template <int D, bool IS_V>
+__device__ __forceinline__ void tile_offsets(int (&off)[Geo<D>::NI_W], int wave, int lane) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int t = 0; t < G::NI_W; ++t) {
+    const int row = (wave * G::NI_W + t) * G::RPI + lane / G::CPR;
+    const int chunk = (lane % G::CPR) ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
+    off[t] = row * G::RB + chunk * 16;
+  }
+}
+
+// Direct global -> LDS copy of one K or V tile (rows key0 .. key0+BN-1) through a buffer
+// resource whose base is the tile's first row and whose size ends at the valid length L: rows
+// at or past L are out of range and arrive as zeros (their scores are masked, so they add
+// exactly nothing), and no load can leave the tensor.
+template <int D>
+__device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0, int L,
+                                          const int (&off)[Geo<D>::NI_W], int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists only for the GPU target
+  using G = Geo<D>;
+  const int bytes = max(L - key0, 0) * G::RB;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(head + (size_t)key0 * D), (short)0, bytes, kBufferFlags);
+#pragma unroll
+  for (int t = 0; t < G::NI_W; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * G::NI_W + t) * 1024, 16, off[t],
+                                             0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); lgkm and exp counters untouched
+}
+
+// Per-lane LDS byte offsets of the fragment reads, fixed for the whole kernel.
+template <int D>
+struct FragAddr {
+  int k[D / 16];  // K row (lane & 31), logical chunk 2c + (lane >> 5), for every c
+  int v[D / 32];  // V transposing read for output block n, keys 4*hh' + (s >> 2)
 };
 
-// Global -> registers for the tile starting at key0.  Keys at or past L are zero-filled, so
-// padded or out-of-range rows never reach the arithmetic (not even as NaN * 0).
-template <class T, int D>
-__device__ __forceinline__ void load_stage(Stage<T>& st, const bf16* Kg, const bf16* Vg, int key0,
-                                           int L, int tid) {
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+template <int D>
+__device__ __forceinline__ FragAddr<D> frag_addr(int lane) {
+  using G = Geo<D>;
+  FragAddr<D> a;
+  const int c32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < T::K_ITERS; ++i) {
-    const int c = tid + i * T::THREADS;
-    const int row = c / T::DC, col = c % T::DC;
-    const int key = key0 + row;
-    st.k[i] = (c < T::K_CHUNKS && key < L)
-                  ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + col * 8)
-                  : zero;
+  for (int c = 0; c < G::KC; ++c) a.k[c] = c32 * G::RB + (((2 * c + hh) ^ G::swz_k(c32)) << 4);
+  const int grp = lane >> 4, s = lane & 15;
+  const int key = 4 * (grp >> 1) + (s >> 2);
+#pragma unroll
+  for (int n = 0; n < G::NB; ++n) {
+    const int dim = n * 32 + 16 * (grp & 1) + 4 * (s & 3);
+    a.v[n] = key * G::RB + (((dim >> 3) ^ G::swz_v(key)) << 4) + ((dim & 7) << 1);
   }
-#pragma unroll
-  for (int i = 0; i < T::V_ITERS; ++i) {
-    const int u = tid + i * T::THREADS;
-    const int quad = u / T::DC, col = u % T::DC;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + quad * 4 + r;
-      st.v[i][r] = (u < T::V_UNITS && key < L)
-                       ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + col * 8)
-                       : zero;
-    }
-  }
+  return a;
 }
 
-// Registers -> LDS.  K keeps its [key][dim] layout.  V is transposed to [dim][key]: each unit
-// of 4 keys x 8 dims becomes 8 runs of 4 keys.  Inside every 16-key group the two middle
-// quads swap places (key quad q goes to position quad ((q & 1) << 1) | (q >> 1)), which is
-// the k-slot order of the score accumulator: lane half 0 holds keys {0-3, 8-11} of the group,
-// half 1 keys {4-7, 12-15}.
-template <class T>
-__device__ __forceinline__ void store_stage(const Stage<T>& st, bf16* buf, int tid) {
-  bf16* Ks = buf;
-  bf16* Vt = buf + T::K_ELEMS;
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// S^T (64 keys x 32 queries of this wave) = K_tile Q^T: 2*D/16 fragment reads and MFMAs.  The
+// reads run kAheadK fragments ahead of the MFMAs that consume them, which hides the LDS
+// latency without holding the whole tile's fragments in registers.
+constexpr int kAheadK = 4;
+template <int D>
+__device__ __forceinline__ void scores(f32x16 (&s)[2], const lds_t* Kb, const FragAddr<D>& fa,
+                                       const bf16x8 (&qf)[D / 16]) {
+  using G = Geo<D>;
+  constexpr int NM = 2 * G::KC;
+  __builtin_amdgcn_sched_barrier(0);
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-  for (int i = 0; i < T::K_ITERS; ++i) {
-    const int c = tid + i * T::THREADS;
-    if (c < T::K_CHUNKS) {
-      const int row = c / T::DC, col = c % T::DC;
-      *reinterpret_cast<u32x4*>(Ks + row * T::KS + col * 8) = st.k[i];
+  for (int c = 0; c < G::KC; ++c) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *reinterpret_cast<const lds_bf16x8*>(Kb + fa.k[c] + kb * 32 * G::RB);
+      s[kb] = mfma32(kf, qf[c], s[kb]);
     }
   }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAheadK, 0);
 #pragma unroll
-  for (int i = 0; i < T::V_ITERS; ++i) {
-    const int u = tid + i * T::THREADS;
-    if (u < T::V_UNITS) {
-      const int quad = u / T::DC, col = u % T::DC;
-      const int qg = quad & 3;
-      const int pos = (quad >> 2) * 16 + ((((qg & 1) << 1) | (qg >> 1)) << 2);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = st.v[i][0][w], x1 = st.v[i][1][w];
-        const uint32_t x2 = st.v[i][2][w], x3 = st.v[i][3][w];
-        u32x2 lo, hi;  // dims 2w and 2w+1, keys 0..3 of the quad
-        lo[0] = (x0 & 0xffffu) | (x1 << 16);
-        lo[1] = (x2 & 0xffffu) | (x3 << 16);
-        hi[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-        hi[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-        const int dim = col * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(Vt + dim * T::VS + pos) = lo;
-        *reinterpret_cast<u32x2*>(Vt + (dim + 1) * T::VS + pos) = hi;
-      }
-    }
+  for (int i = 0; i < NM - kAheadK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadK, 0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL, int QB, int NW>
-__global__ void __launch_bounds__(64 * NW) fwd_bf16_kernel(Params p) {
-  using T = Tile<D, QB, NW>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::BUF];
+// O^T (d x 32 queries) += V_tile^T P^T: 4*D/32 MFMAs, each fed by two transposing reads, which
+// run kAheadV MFMAs ahead.
+constexpr int kAheadV = 4;
+template <int D>
+__device__ __forceinline__ void pv(f32x16 (&acc)[D / 32], const lds_t* Vb, const FragAddr<D>& fa,
+                                   const bf16x8 (&pf)[4]) {
+  using G = Geo<D>;
+  constexpr int NM = 4 * G::NB;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+      const lds_t* p = Vb + fa.v[n] + jj * 16 * G::RB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * G::RB));
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[n] = mfma32(vf, pf[jj], acc[n]);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAheadV, 0);
+#pragma unroll
+  for (int i = 0; i < NM - kAheadV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadV, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Masks the scores a query row may not see: keys at or past L, and (causal) keys after it.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int key0, int L, int qrow, int hh) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool ok = key < L && (!CAUSAL || key <= qrow);
+      if (!ok) s[kb][r] = kNegInf;
+    }
+}
+
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+  float m0 = s[0][0], m1 = s[1][0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) {
+    m0 = fmaxf(m0, s[0][r]);
+    m1 = fmaxf(m1, s[1][r]);
+  }
+  return max_xor32(fmaxf(m0, m1));
+}
+
+// Probabilities of one tile, exp2(s * sl2 - m), packed to bf16 in the k-slot order of the
+// P^T operand; returns their sum over this lane's 32 keys.  On masked tiles a masked score
+// (-inf) gives exactly 0 even when the scale is 0 (where -inf * 0 would be NaN).
+template <bool MASKED>
+__device__ __forceinline__ float probs(bf16x8 (&pf)[4], const f32x16 (&s)[2], float sl2,
+                                       float m_use) {
+  float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float e[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float x = s[jj >> 1][8 * (jj & 1) + t];
+      float arg = fmaf(x, sl2, -m_use);
+      if (MASKED && x == kNegInf) arg = kNegInf;
+      e[t] = fast_exp2(arg);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      rs0 += e[t];
+      rs1 += e[t + 1];
+    }
+    pf[jj] = pack_bf16x8(e);
+  }
+  return rs0 + rs1;
+}
+
+template <int D, bool CAUSAL, bool PIPE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_bf16_kernel(Params p) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) char k0s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[G::TILE];
+  lds_t* const K0 = (lds_t*)k0s;
+  lds_t* const K1 = (lds_t*)k1s;
+  lds_t* const V0 = (lds_t*)v0s;
+  lds_t* const V1 = (lds_t*)v1s;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -161,7 +293,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_bf16_kernel(Params p) {
   int L = N;
   if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
 
-  const int q0 = qt * T::BM;
+  const int q0 = qt * kBM;
   const bf16* Qg = p.q + (size_t)bh * N * D;
   const bf16* Kg = p.k + (size_t)(b * p.Hkv + g) * N * D;
   const bf16* Vg = p.v + (size_t)(b * p.Hkv + g) * N * D;
@@ -169,172 +301,164 @@ __global__ void __launch_bounds__(64 * NW) fwd_bf16_kernel(Params p) {
   float* LSEg = p.lse + (size_t)bh * N;
 
   if (q0 >= L) {  // every row of this tile is padding: O = 0, LSE = -inf
-    const int rows = min(T::BM, N - q0);
+    const int rows = min(kBM, N - q0);
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < rows * T::DC; i += T::THREADS)
+    for (int i = tid; i < rows * G::CPR; i += kThreads)
       *reinterpret_cast<u32x4*>(Og + (size_t)q0 * D + i * 8) = zero;
-    for (int r = tid; r < rows; r += T::THREADS) LSEg[q0 + r] = kNegInf;
+    for (int r = tid; r < rows; r += kThreads) LSEg[q0 + r] = kNegInf;
     return;
   }
 
-  const int kv_end = CAUSAL ? min(L, q0 + T::BM) : L;
-  const int n_kt = (kv_end + T::BN - 1) / T::BN;
-  const int qw0 = q0 + wave * T::WQ;
+  const int kv_end = CAUSAL ? min(L, q0 + kBM) : L;   // keys this workgroup needs
+  const int n_kt = (kv_end + kBN - 1) / kBN;
+  const int qw0 = q0 + wave * kWQ;
+  const int qrow = qw0 + c32;
+  // Tiles this wave needs (fewer than n_kt on the causal diagonal).
+  const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
   const float sl2 = p.sl2;
+  int koff[G::NI_W], voff[G::NI_W];
+  tile_offsets<D, false>(koff, wave, lane);
+  tile_offsets<D, true>(voff, wave, lane);
+
+  // Issue the first loads before anything else: K_0, V_0 (and K_1 when pipelined).
+  load_tile<D>(K0, Kg, 0, L, koff, wave);
+  load_tile<D>(V0, Vg, 0, L, voff, wave);
+  if (PIPE && n_kt > 1) load_tile<D>(K1, Kg, kBN, L, koff, wave);
 
   // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel.
-  bf16x8 qf[QB][T::KC];
+  bf16x8 qf[G::KC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + c32;
-#pragma unroll
-    for (int c = 0; c < T::KC; ++c) {
-      if (row < N) {
-        qf[qb][c] = *reinterpret_cast<const bf16x8*>(Qg + (size_t)row * D + c * 16 + hh * 8);
-      } else {
-        qf[qb][c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      }
-    }
+  for (int c = 0; c < G::KC; ++c) {
+    qf[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
+                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
+  const FragAddr<D> fa = frag_addr<D>(lane);
 
-  float m_run[QB], l_run[QB];
-  f32x16 acc[T::NB][QB];
+  f32x16 acc[G::NB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = kNegInf;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int n = 0; n < T::NB; ++n) acc[n][qb] = f32x16{};
-  }
+  for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
+  float m_run = kNegInf;  // reference maximum (log2 units); -inf until a key is seen
+  float l_run = 0.f;      // this lane's share of the row sum (relative to m_run)
 
-  Stage<T> st;
-  load_stage<T, D>(st, Kg, Vg, 0, L, tid);
-  store_stage<T>(st, smem, tid);
+  f32x16 sA[2], sB[2];
+  wait_loads();
   __syncthreads();
-  if (n_kt > 1) load_stage<T, D>(st, Kg, Vg, T::BN, L, tid);
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int key0 = kt * T::BN;
-    const bf16* Ks = smem + (kt & 1) * T::BUF;
-    const bf16* Vt = Ks + T::K_ELEMS;
-    if (!CAUSAL || key0 <= qw0 + T::WQ - 1) {
-      const bool masked = (key0 + T::BN > L) || (CAUSAL && key0 + T::BN - 1 > qw0);
-
-      // S^T[key][query] for the 64 keys of the tile (two 32-key blocks).
-      f32x16 s[2][QB];
+  // Row statistics of a fresh score tile: mask (only on tiles that need it), row maximum and
+  // the lazy rescale.  The rescale branch is wave-uniform and rare.
+  auto row_max = [&](f32x16 (&s)[2], int key0, auto masked) {
+    if constexpr (decltype(masked)::value) mask_scores<CAUSAL>(s, key0, L, qrow, hh);
+    const float mx = tile_max(s);
+    return (mx == kNegInf) ? kNegInf : mx * sl2;
+  };
+  auto rescale = [&](float mt) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < T::KC; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + c32) * T::KS + c * 16 + hh * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(kf, qf[qb][c], s[kb][qb]);
-        }
-      }
-
-      // Online softmax: running max m (base-2 exponent units), running sum l, rescale.
-      bf16x8 pf[QB][4];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (masked) {
-          const int qrow = qw0 + qb * 32 + c32;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool ok = key < L && (!CAUSAL || key <= qrow);
-              if (!ok) s[kb][qb][r] = kNegInf;
-            }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = max_xor32(mx);
-        const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - m_use);
-        m_run[qb] = m_new;
-        float pv[32];
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float x = s[kb][qb][r];
-            float e = fast_exp2(fmaf(x, sl2, -m_use));
-            if (masked && x == kNegInf) e = 0.f;
-            pv[kb * 16 + r] = e;
-            rs += e;
-          }
-        l_run[qb] = fmaf(alpha, l_run[qb], rs);
-#pragma unroll
-        for (int n = 0; n < T::NB; ++n) acc[n][qb] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pf[qb][j] = pack_bf16x8(&pv[8 * j]);
-      }
-
-      // O^T[dim][query] += V^T[dim][key] P^T[key][query].
-#pragma unroll
-      for (int n = 0; n < T::NB; ++n) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(Vt + (n * 32 + c32) * T::VS + j * 16 + hh * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[n][qb] = mfma32(vf, pf[qb][j], acc[n][qb]);
-        }
-      }
+      for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
+      m_run = m_new;
     }
-    if (kt + 1 < n_kt) {
-      store_stage<T>(st, smem + ((kt + 1) & 1) * T::BUF, tid);
-      if (kt + 2 < n_kt) load_stage<T, D>(st, Kg, Vg, (kt + 2) * T::BN, L, tid);
+  };
+  auto needs_mask = [&](int key0) {
+    return (key0 + kBN > L) || (CAUSAL && key0 + kBN - 1 > qw0);
+  };
+
+  if constexpr (PIPE) {
+    scores<D>(sA, K0, fa, qf);
+    rescale(needs_mask(0) ? row_max(sA, 0, std::true_type{}) : row_max(sA, 0, std::false_type{}));
+
+    // Iteration j: S_{j+1} = Q K_{j+1}^T and P_j = exp2(S_j - m); then O += V_j P_j and the
+    // row maxima of S_{j+1}; V_{j+1} and K_{j+2} load meanwhile.  With no branch between them,
+    // the matrix instructions of one part and the vector instructions of the other are
+    // scheduled together.  Buffers alternate, so the body is instantiated for even and odd j,
+    // keeping every LDS access on a fixed buffer.
+    auto body = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], lds_t* Kn, lds_t* Vc, lds_t* Vn,
+                    lds_t* Kf) {
+      if (j + 1 < n_kt) load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
+      if (j + 2 < n_kt) load_tile<D>(Kf, Kg, (j + 2) * kBN, L, koff, wave);
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      if (j + 1 < n_kw) {
+        const int key1 = (j + 1) * kBN;
+        float mt;
+        bf16x8 pf[4];
+        if (needs_mask(key1)) {
+          scores<D>(sn, Kn, fa, qf);
+          l_run += probs<true>(pf, sc, sl2, m_use);
+          pv<D>(acc, Vc, fa, pf);
+          mt = row_max(sn, key1, std::true_type{});
+        } else {
+          scores<D>(sn, Kn, fa, qf);
+          l_run += probs<true>(pf, sc, sl2, m_use);
+          pv<D>(acc, Vc, fa, pf);
+          mt = row_max(sn, key1, std::false_type{});
+        }
+        rescale(mt);
+      } else if (j < n_kw) {
+        bf16x8 pf[4];
+        l_run += probs<true>(pf, sc, sl2, m_use);
+        pv<D>(acc, Vc, fa, pf);
+      }
+      wait_loads();
+      __syncthreads();
+    };
+    for (int j = 0; j < n_kt; j += 2) {
+      body(j, sA, sB, K1, V0, V1, K0);
+      if (j + 1 < n_kt) body(j + 1, sB, sA, K0, V1, V0, K1);
     }
-    __syncthreads();
+  } else {
+    // Iteration j: S_j = Q K_j^T, row maxima, P_j, O += V_j P_j, while K_{j+1} and V_{j+1}
+    // load into the other buffers.  The overlap of matrix and vector work comes from the
+    // second workgroup on each SIMD.
+    auto body = [&](int j, lds_t* Kc, lds_t* Vc, lds_t* Kn, lds_t* Vn) {
+      if (j + 1 < n_kt) {
+        load_tile<D>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
+        load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
+      }
+      if (j < n_kw) {
+        const int key0 = j * kBN;
+        auto tile = [&](auto masked) {
+          constexpr bool M = decltype(masked)::value;
+          scores<D>(sA, Kc, fa, qf);
+          rescale(row_max(sA, key0, masked));
+          bf16x8 pf[4];
+          l_run += probs<M>(pf, sA, sl2, m_run == kNegInf ? 0.f : m_run);
+          pv<D>(acc, Vc, fa, pf);
+        };
+        if (needs_mask(key0)) tile(std::true_type{});
+        else tile(std::false_type{});
+      }
+      wait_loads();
+      __syncthreads();
+    };
+    for (int j = 0; j < n_kt; j += 2) {
+      body(j, K0, V0, K1, V1);
+      if (j + 1 < n_kt) body(j + 1, K1, V1, K0, V0);
+    }
   }
 
   // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
+  const float lt = add_xor32(l_run);
+  if (qrow < N) {
+    const bool valid = qrow < L;
+    const float inv = valid ? 1.f / lt : 0.f;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = add_xor32(l_run[qb]);
-    const int row = qw0 + qb * 32 + c32;
-    if (row < N) {
-      const bool valid = row < L;
-      const float inv = valid ? 1.f / lt : 0.f;
+    for (int n = 0; n < G::NB; ++n) {
 #pragma unroll
-      for (int n = 0; n < T::NB; ++n) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          float x[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[j] = valid ? acc[n][qb][4 * r4 + j] * inv : 0.f;
-          u32x2 w;
-          w[0] = pack_bf16x2(x[0], x[1]);
-          w[1] = pack_bf16x2(x[2], x[3]);
-          *reinterpret_cast<u32x2*>(Og + (size_t)row * D + n * 32 + 8 * r4 + 4 * hh) = w;
-        }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[n][4 * r4 + 0] * inv, acc[n][4 * r4 + 1] * inv);
+        w[1] = pack_bf16x2(acc[n][4 * r4 + 2] * inv, acc[n][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(Og + (size_t)qrow * D + n * 32 + 8 * r4 + 4 * hh) = w;
       }
-      if (hh == 0) LSEg[row] = valid ? (m_run[qb] + __log2f(lt)) * kLn2 : kNegInf;
     }
+    if (hh == 0) LSEg[qrow] = valid ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
   }
 }
 
-// Tile shape chosen for gfx950: 4 waves x 32 query rows, 64-key tiles, ~70 KB of LDS per
-// workgroup (two workgroups fit in a CU's 160 KB).
-constexpr int kQB = 1;
-constexpr int kNW = 4;
-
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PIPE = kPipe>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  using T = Tile<D, kQB, kNW>;
   Params p;
   p.q = static_cast<const bf16*>(a.q);
   p.k = static_cast<const bf16*>(a.k);
@@ -346,17 +470,14 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.group = a.H / a.Hkv;
   p.Hkv = a.Hkv;
   p.N = a.N;
-  p.n_qt = (a.N + T::BM - 1) / T::BM;
+  p.n_qt = (a.N + kBM - 1) / kBM;
   p.total = a.B * a.H * p.n_qt;
   p.sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, kQB, kNW>), dim3(p.total), dim3(T::THREADS), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PIPE>), dim3(p.total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
-
-int fwd_bf16_rows_per_workgroup() { return Tile<128, kQB, kNW>::BM; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
