@@ -17,6 +17,7 @@ Prints ONE JSON line.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +29,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (% MFMA peak) at N=16384,d=128; decode GB/s (% HBM)"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _profiled_traffic(kernel):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json), or None when
+    the kernel's source has changed since the counters were taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    with open(PROFILE_TRAFFIC) as f:
+        entry = json.load(f).get(kernel)
+    if not entry:
+        return None
+    with open(os.path.join(ROOT, entry["source"]), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    return entry["hbm_bytes_per_launch"] if digest == entry["source_sha256_16"] else None
 
 
 def _events(torch):
@@ -198,14 +213,8 @@ def main():
     dbytes = acc.decode_bytes(lens_host, wd["Hq"], wd["Hkv"], wd["d"], wd["block_size"])
     gbps = dbytes / (t_dec * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        with open(PROFILE_TRAFFIC) as f:
-            tr = json.load(f)
-        traffic = tr.get("fwd_bf16_kernel", {}).get("hbm_bytes_per_launch")
-        dec_traffic = tr.get("decode_split_kernel", {}).get("hbm_bytes_per_launch")
-    else:
-        dec_traffic = None
+    traffic = _profiled_traffic("fwd")
+    dec_traffic = _profiled_traffic("decode")
 
     out = {
         "metric": METRIC,
