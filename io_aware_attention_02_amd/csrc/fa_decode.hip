@@ -3,13 +3,12 @@
 // The cache is a pool of physical blocks of 16 tokens, [num_blocks][16][Hkv][d]; a block
 // table maps each sequence's logical blocks to physical ones.  Following the non-contiguous
 // block gather page (ocdem.com, vLLM PagedAttention rework):
-//  * §二.3 -- the block ids a workgroup will visit are loaded into registers up front (one id
-//    per lane) and broadcast from there, so no gather waits on the index array;
-//  * §二.1 -- each block's keys and values are gathered with coalesced loads (16 lanes cover one
-//    256-byte token row) into on-chip memory, then read from there in the layout the matrix
-//    cores want (values transposed on the way in);
+//  * §二.3 -- the block ids a wave will visit are loaded into registers up front (one id per
+//    lane) and read from there into scalar registers, so no gather waits on the index array;
+//  * §二.1 -- each block's values are gathered with coalesced direct loads into on-chip memory
+//    (a ring of stages), and read from there in the layout the matrix cores want;
 //  * §二.4 -- gather and attention are one kernel: scores against the register-resident query,
-//    online softmax and the probability-weighted sum of values follow each gathered tile.
+//    online softmax and the probability-weighted sum of values follow each gathered block.
 // Load balance (§二.2 asks for dynamic balancing of unequal per-query work): instead of a
 // per-warp task queue, each sequence's tokens are cut into fixed 512-token ranges, one wave
 // each, so work per wave is equal whatever the length mix.  Each range writes its partial
@@ -17,21 +16,34 @@
 // rule of the online softmax ("FlashAttention优化" §3.2.2: the result is the same for any
 // block order and grouping).
 //
-// CDNA4 mapping: the Hq/Hkv query heads that share kv head g form the 16 columns of
-// v_mfma_f32_16x16x32_bf16 (unused columns are zero).  Scores are S^T = K Q^T (tokens in
-// rows, heads in columns); the score accumulator of a lane is already the B operand of
-// O^T += V^T P^T, so probabilities stay in registers.  32 tokens (two physical blocks) are
-// processed per step; the next step's gathers are in flight while the current one computes.
+// CDNA4 mapping:
+//  * The Hq/Hkv query heads sharing kv head g are the 16 columns of the matrix-core tiles
+//    (unused columns are zero).  Scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16; P^T is the
+//    score accumulator packed to bf16, the B operand of O^T += V^T P^T
+//    (v_mfma_f32_16x16x16_bf16), so probabilities never leave registers.
+//  * K needs no on-chip staging: each lane loads its A-operand fragment (one token row, a
+//    quarter of the head dimension, 16-byte loads) straight into registers.  The head
+//    dimension is contracted in a permuted order that the query fragments share.
+//  * V goes from global memory straight into LDS (buffer_load ... lds, 16 bytes per lane,
+//    chunks XOR-swizzled by row) and its V^T fragments are read with ds_read_b64_tr_b16.
+//  * Every load is issued kStages-1 blocks ahead of its use through a per-block buffer
+//    resource whose size ends at the sequence length: cache slots past the length read as
+//    zeros (never as whatever the pool holds there) and no load leaves the block.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
+typedef __attribute__((address_space(3))) char lds_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 constexpr int kBS = 16;                         // tokens per physical block
-constexpr int kStepTok = 32;                    // tokens per pipeline step (two blocks)
-constexpr int kSplit = kDecodeSplitTokens;      // tokens per workgroup
-constexpr int kBlocksPerSplit = kSplit / kBS;   // block ids prefetched per workgroup (<= 64)
+constexpr int kSplit = kDecodeSplitTokens;      // tokens per wave
+constexpr int kBlocksPerSplit = kSplit / kBS;   // block ids prefetched per wave (<= 64)
+constexpr int kStages = 4;                      // blocks in the load ring
+constexpr int kBufferFlags = 0x00020000;        // buffer resource word 3: 32-bit data, raw
 static_assert(kBlocksPerSplit <= 64, "one block id per lane");
 
 struct DecodeParams {
@@ -50,88 +62,74 @@ struct DecodeParams {
 };
 
 template <int D>
-struct DTile {
-  static constexpr int CPR = D / 8;            // 16-byte chunks per token row
-  static constexpr int RPI = 64 / CPR;         // token rows per load instruction
-  static constexpr int TPL = kBS / RPI;        // rows per lane per block (consecutive tokens)
-  static constexpr int KS = D + 8;             // LDS row stride of K (elements)
-  static constexpr int VS = kStepTok + 8;      // LDS row stride of transposed V (elements)
-  static constexpr int NB = D / 16;            // 16-dim blocks of the output
-  static constexpr int KC = D / 32;            // 32-dim chunks of the score contraction
+struct DGeo {
+  static constexpr int RB = D * 2;              // bytes of one token's head row
+  static constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  static constexpr int VTILE = kBS * RB;        // bytes of one block's V for one kv head
+  static constexpr int NDMA = VTILE / 1024;     // 1 KB direct loads per block
+  static constexpr int RPI = 1024 / RB;         // rows per direct load
+  static constexpr int KC = D / 32;             // 16x16x32 MFMAs of the score contraction
+  static constexpr int NB = D / 16;             // 16-dim output blocks
+  static constexpr int QD = D / 4;              // head dims held by one lane group
+  // V chunk swizzle: the 16 rows x 32 bytes of one transposing read hit every bank group
+  // exactly twice.
+  __device__ static int swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
+};
+
+// Scalar state of one block: its buffer resources for K and V.
+struct BlockRes {
+  __amdgpu_buffer_rsrc_t k, v;
 };
 
 template <int D>
-struct DStage {
-  u32x4 k[2][DTile<D>::TPL];
-  u32x4 v[2][DTile<D>::TPL];
-};
-
-// Gather the two blocks of one step into registers.  Lane l covers chunk (l % CPR) of token
-// rows TPL*(l / CPR) .. +TPL-1 of each block; tokens at or past L are zero-filled.
-template <int D>
-__device__ __forceinline__ void gather_step(DStage<D>& st, const DecodeParams& p, int bid0,
-                                            int bid1, int tok0, int L, int g, int lane) {
-  using T = DTile<D>;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int col = lane % T::CPR, rg = lane / T::CPR;
-  const size_t row_stride = (size_t)p.Hkv * D;
-#pragma unroll
-  for (int bi = 0; bi < 2; ++bi) {
-    const int bid = bi ? bid1 : bid0;
-    const bf16* kb = p.kc + (size_t)bid * kBS * row_stride + (size_t)g * D + col * 8;
-    const bf16* vb = p.vc + (size_t)bid * kBS * row_stride + (size_t)g * D + col * 8;
-#pragma unroll
-    for (int i = 0; i < T::TPL; ++i) {
-      const int row = rg * T::TPL + i;
-      const bool ok = tok0 + bi * kBS + row < L;
-      st.k[bi][i] = ok ? *reinterpret_cast<const u32x4*>(kb + row * row_stride) : zero;
-      st.v[bi][i] = ok ? *reinterpret_cast<const u32x4*>(vb + row * row_stride) : zero;
-    }
-  }
+__device__ __forceinline__ BlockRes block_res(const DecodeParams& p, int bid, int valid_rows,
+                                              int row_bytes) {
+  const size_t base = (size_t)bid * kBS * p.Hkv * D;
+  const int bytes = valid_rows * row_bytes;  // 0 for a block past the range
+  BlockRes r;
+  r.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p.kc + base), (short)0, bytes,
+                                          kBufferFlags);
+  r.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p.vc + base), (short)0, bytes,
+                                          kBufferFlags);
+  return r;
 }
 
-// Registers -> LDS.  K keeps [token][dim].  V goes to [dim][position] where token
-// 16*bi + 4*h + j sits at position 8*h + 4*bi + j: the k-slot order in which a lane of the
-// score accumulator holds its probabilities.
 template <int D>
-__device__ __forceinline__ void stage_to_lds(const DStage<D>& st, bf16* Ks, bf16* Vt, int lane) {
-  using T = DTile<D>;
-  const int col = lane % T::CPR, rg = lane / T::CPR;
+struct KFrag {
+  bf16x8 c[DGeo<D>::KC];
+};
+
+// Issue one block's loads: K fragments into registers, V into LDS stage `vs`.
+template <int D>
+__device__ __forceinline__ void issue_block(KFrag<D>& kf, lds_t* vs, const BlockRes& r,
+                                            int koff, const int (&voff)[DGeo<D>::NDMA]) {
+  using G = DGeo<D>;
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi) {
+  for (int c = 0; c < G::KC; ++c)
+    kf.c[c] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k, koff + 16 * c, 0, 0));
 #pragma unroll
-    for (int i = 0; i < T::TPL; ++i)
-      *reinterpret_cast<u32x4*>(Ks + (bi * kBS + rg * T::TPL + i) * T::KS + col * 8) = st.k[bi][i];
-    const int t0 = rg * T::TPL;                      // first token of this lane in the block
-    const int pos = 8 * (t0 >> 2) + 4 * bi + (t0 & 3);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int dim = col * 8 + 2 * w;
-      if constexpr (T::TPL == 4) {
-        const uint32_t x0 = st.v[bi][0][w], x1 = st.v[bi][1][w];
-        const uint32_t x2 = st.v[bi][2][w], x3 = st.v[bi][3][w];
-        u32x2 lo, hi;
-        lo[0] = (x0 & 0xffffu) | (x1 << 16);
-        lo[1] = (x2 & 0xffffu) | (x3 << 16);
-        hi[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-        hi[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(Vt + dim * T::VS + pos) = lo;
-        *reinterpret_cast<u32x2*>(Vt + (dim + 1) * T::VS + pos) = hi;
-      } else {
-        static_assert(T::TPL == 2, "head dim 64 or 128");
-        const uint32_t x0 = st.v[bi][0][w], x1 = st.v[bi][1][w];
-        *reinterpret_cast<uint32_t*>(Vt + dim * T::VS + pos) = (x0 & 0xffffu) | (x1 << 16);
-        *reinterpret_cast<uint32_t*>(Vt + (dim + 1) * T::VS + pos) = (x0 >> 16) | (x1 & 0xffff0000u);
-      }
-    }
-  }
+  for (int t = 0; t < G::NDMA; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, vs + t * 1024, 16, voff[t], 0, 0, 0);
+}
+
+// vmcnt(n): wait until at most n vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
 template <int D>
 __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
-  using T = DTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kStepTok * T::KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * T::VS];
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only for the GPU target
+  using G = DGeo<D>;
+  __shared__ __attribute__((aligned(1024))) char vs0[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char vs2[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char vs3[G::VTILE];
+  lds_t* const VS[kStages] = {(lds_t*)vs0, (lds_t*)vs1, (lds_t*)vs2, (lds_t*)vs3};
+  constexpr int kLoadsPerBlock = G::KC + G::NDMA;
 
   const int lane = threadIdx.x;
   const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z;
@@ -139,64 +137,83 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
   const int tok_begin = sp * kSplit;
   if (tok_begin >= L) return;
   const int tok_end = min(L, tok_begin + kSplit);
-  const int n_steps = (tok_end - tok_begin + kStepTok - 1) / kStepTok;
   const int blk_begin = tok_begin / kBS;
   const int n_blk = (tok_end - tok_begin + kBS - 1) / kBS;
 
   // Block ids of this range, one per lane (index prefetch into registers).
   const int my_bid = lane < n_blk ? p.table[(size_t)b * p.max_blocks + blk_begin + lane] : 0;
 
-  // Query fragments: B operand of S^T = K Q^T, column = head (l & 15), k-slots 8*(l >> 4).
-  const int head = lane & 15, hq = lane >> 4;
-  const bool head_ok = head < p.group;
-  const int qh = g * p.group + head;
-  bf16x8 qf[T::KC];
+  const int row_bytes = p.Hkv * G::RB;
+  const int col = lane & 15, grp = lane >> 4;
+  // K: lane holds token `col`, head dims QD*grp .. +QD-1 (16 bytes per MFMA step).
+  const int koff = col * row_bytes + (g * D + G::QD * grp) * 2;
+  // V: direct load t writes LDS rows RPI*t .. +RPI-1; lane -> (row, swizzled chunk).
+  int voff[G::NDMA];
 #pragma unroll
-  for (int c = 0; c < T::KC; ++c) {
-    qf[c] = head_ok ? *reinterpret_cast<const bf16x8*>(p.q + ((size_t)b * p.Hq + qh) * D + c * 32 + hq * 8)
-                    : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  for (int t = 0; t < G::NDMA; ++t) {
+    const int row = t * G::RPI + lane / G::CPR;
+    const int chunk = (lane % G::CPR) ^ G::swz(row);
+    voff[t] = row * row_bytes + g * G::RB + chunk * 16;
+  }
+  // V^T fragment reads: group grp reads tokens 4*grp .. +3, dims 16n + 4*(s & 3) per source
+  // lane s; the 16 lanes then hold 4 tokens of dims 16n .. 16n+15.
+  int vrd[G::NB];
+  {
+    const int s = lane & 15;
+    const int row = 4 * grp + (s >> 2);
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+      const int dim = 16 * n + 4 * (s & 3);
+      vrd[n] = row * G::RB + (((dim >> 3) ^ G::swz(row)) << 4) + ((dim & 7) << 1);
+    }
   }
 
-  f32x4 acc[T::NB];
+  // Query fragments: B operand of S^T = K Q^T, column = head `col`, the same dims as K.
+  const bool head_ok = col < p.group;
+  const int qh = g * p.group + col;
+  bf16x8 qf[G::KC];
 #pragma unroll
-  for (int n = 0; n < T::NB; ++n) acc[n] = f32x4{};
+  for (int c = 0; c < G::KC; ++c) {
+    qf[c] = head_ok
+                ? *reinterpret_cast<const bf16x8*>(p.q + ((size_t)b * p.Hq + qh) * D + G::QD * grp + 8 * c)
+                : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  auto res_of = [&](int i) __attribute__((always_inline)) {  // scalar resources of block i of the range (empty past the end)
+    const int bid = __builtin_amdgcn_readlane(my_bid, min(i, n_blk - 1));
+    const int valid = i < n_blk ? min(kBS, tok_end - (tok_begin + i * kBS)) : 0;
+    return block_res<D>(p, bid, valid, row_bytes);
+  };
+
+  f32x4 acc[G::NB];
+#pragma unroll
+  for (int n = 0; n < G::NB; ++n) acc[n] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
   const float sl2 = p.sl2;
 
-  auto bid_at = [&](int i) {  // broadcast block id i of the range (clamped for a tail step)
-    return __shfl(my_bid, min(i, n_blk - 1), 64);
-  };
-
-  DStage<D> cur, nxt;
-  gather_step<D>(cur, p, bid_at(0), bid_at(1), tok_begin, L, g, lane);
-  for (int s = 0; s < n_steps; ++s) {
-    const int tok0 = tok_begin + s * kStepTok;
-    if (s + 1 < n_steps)
-      gather_step<D>(nxt, p, bid_at(2 * s + 2), bid_at(2 * s + 3), tok0 + kStepTok, L, g, lane);
-    __syncthreads();  // previous step's LDS reads are done
-    stage_to_lds<D>(cur, Ks, Vt, lane);
-    __syncthreads();
-
-    // Scores for the two blocks: lane holds head (l & 15), tokens 16*bi + 4*(l >> 4) + j.
-    f32x4 s2[2];
+  KFrag<D> kf[kStages];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      s2[bi] = f32x4{};
+  for (int i = 0; i < kStages - 1; ++i) issue_block<D>(kf[i], VS[i], res_of(i), koff, voff);
+
+  // Block i lives in stage i % kStages; issuing block i + kStages - 1 before computing block i
+  // keeps kStages - 1 blocks of loads in flight.  Past the end the loads are empty (size 0) but
+  // still issued, so the wait count below is the same on every step.
+  auto step = [&](int i, auto stage) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr int NX = (ST + kStages - 1) % kStages;
+    issue_block<D>(kf[NX], VS[NX], res_of(i + kStages - 1), koff, voff);
+    wait_vmem<(kStages - 1) * kLoadsPerBlock>();
+    if (i >= n_blk) return;
+    f32x4 s = f32x4{};
 #pragma unroll
-      for (int c = 0; c < T::KC; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (bi * kBS + head) * T::KS + c * 32 + hq * 8);
-        s2[bi] = mfma16k32(kf, qf[c], s2[bi]);
-      }
+    for (int c = 0; c < G::KC; ++c) s = mfma16k32(kf[ST].c[c], qf[c], s);
+    const int tok0 = tok_begin + i * kBS;
+    if (tok0 + kBS > L) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (tok0 + 4 * grp + r >= L) s[r] = kNegInf;
     }
-    const bool masked = tok0 + kStepTok > L;
-    float mx = kNegInf;
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (masked && tok0 + bi * kBS + 4 * hq + j >= L) s2[bi][j] = kNegInf;
-        mx = fmaxf(mx, s2[bi][j]);
-      }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = max_xor32(mx);
     const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
@@ -204,45 +221,51 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
-    float pv[8];
-    float rs = 0.f;
+    float e[4];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = s2[bi][j];
-        float e = fast_exp2(fmaf(x, sl2, -m_use));
-        if (masked && x == kNegInf) e = 0.f;
-        pv[4 * bi + j] = e;
-        rs += e;
-      }
-    l_run = fmaf(alpha, l_run, rs);
-    const bf16x8 pf = pack_bf16x8(pv);
-#pragma unroll
-    for (int n = 0; n < T::NB; ++n) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (n * 16 + head) * T::VS + hq * 8);
-      acc[n] = mfma16k32(vf, pf, acc[n] * alpha);
+    for (int r = 0; r < 4; ++r) {
+      float arg = fmaf(s[r], sl2, -m_use);
+      if (s[r] == kNegInf) arg = kNegInf;  // exactly 0, also when the scale is 0
+      e[r] = fast_exp2(arg);
     }
-    cur = nxt;
+    l_run = fmaf(alpha, l_run, (e[0] + e[1]) + (e[2] + e[3]));
+    u32x2 pk;
+    pk[0] = pack_bf16x2(e[0], e[1]);
+    pk[1] = pack_bf16x2(e[2], e[3]);
+    const bf16x4 pf = __builtin_bit_cast(bf16x4, pk);
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+      const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(VS[ST] + vrd[n]));
+      acc[n] = mfma16k16(__builtin_bit_cast(bf16x4, v), pf, acc[n] * alpha);
+    }
+  };
+  for (int i = 0; i < n_blk; i += kStages) {
+    step(i + 0, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
+    step(i + 2, std::integral_constant<int, 2>{});
+    step(i + 3, std::integral_constant<int, 3>{});
   }
+  wait_vmem<0>();  // no direct load may still target this wave's LDS when it exits
 
-  // Partial results of this range: lane (head, hq) holds dims 16*n + 4*hq + j.
+  // Partial results of this range: lane (head col, grp) holds dims 16n + 4*grp + r.
   float lt = l_run + shfl_xor(l_run, 16);
   lt = add_xor32(lt);
   if (head_ok) {
     const size_t slot = ((size_t)b * p.Hq + qh) * p.MS + sp;
 #pragma unroll
-    for (int n = 0; n < T::NB; ++n)
-      *reinterpret_cast<f32x4*>(p.opart + slot * D + n * 16 + 4 * hq) = acc[n];
-    if (hq == 0) {
+    for (int n = 0; n < G::NB; ++n)
+      *reinterpret_cast<f32x4*>(p.opart + slot * D + 16 * n + 4 * grp) = acc[n];
+    if (grp == 0) {
       p.mpart[slot] = m_run;
       p.lpart[slot] = lt;
     }
   }
+#endif
 }
 
 // Merge the ranges of one (sequence, query head): M = max m_s, w_s = 2^(m_s - M),
-// O = sum w_s O_s / sum w_s l_s, LSE = ln 2 * (M + log2 sum w_s l_s).
+// O = sum w_s O_s / sum w_s l_s, LSE = ln 2 * (M + log2 sum w_s l_s).  Lane s holds range s's
+// statistics; the weighted sum over ranges is unrolled so that its loads overlap.
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeParams p) {
   constexpr int DPL = D / 64;  // dims per lane
@@ -252,27 +275,63 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeParams p) {
   const int n = (L + kSplit - 1) / kSplit;
   const size_t base = ((size_t)b * p.Hq + h) * p.MS;
   bf16* out = p.o + ((size_t)b * p.Hq + h) * D + lane * DPL;
-  float M = kNegInf;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, p.mpart[base + s]);
+  if (n == 0) {
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out[j] = static_cast<bf16>(0.f);
+    if (p.lse != nullptr && lane == 0) p.lse[(size_t)b * p.Hq + h] = kNegInf;
+    return;
+  }
   float num[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) num[j] = 0.f;
-  float den = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float w = fast_exp2(p.mpart[base + s] - M);
-    den = fmaf(w, p.lpart[base + s], den);
-    const float* src = p.opart + (base + s) * D + lane * DPL;
+  float M = kNegInf, den = 0.f;
+  // Ranges are taken 64 at a time (one per lane); a sequence has at most MS of them.
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int s = s0 + lane;
+    const float ms = s < n ? p.mpart[base + s] : kNegInf;
+    const float ls = s < n ? p.lpart[base + s] : 0.f;
+    float mx = ms;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) num[j] = fmaf(w, src[j], num[j]);
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const float M_new = fmaxf(M, mx);
+    const float scale_old = fast_exp2(M - M_new);  // 0 on the first chunk (M = -inf)
+    const float w = s < n ? fast_exp2(ms - M_new) : 0.f;
+    float c = w * ls;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+    den = fmaf(den, scale_old, c);
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) num[j] *= scale_old;
+    const int cnt = min(64, n - s0);
+    int t = 0;
+    for (; t + 4 <= cnt; t += 4) {
+      float x[4][DPL];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) x[u][j] = p.opart[(base + s0 + t + u) * D + lane * DPL + j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = __shfl(w, t + u, 64);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) num[j] = fmaf(wu, x[u][j], num[j]);
+      }
+    }
+    for (; t < cnt; ++t) {
+      const float wu = __shfl(w, t, 64);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) num[j] = fmaf(wu, p.opart[(base + s0 + t) * D + lane * DPL + j], num[j]);
+    }
+    M = M_new;
   }
-  const float inv = n > 0 ? 1.f / den : 0.f;
+  const float inv = 1.f / den;
   if constexpr (DPL == 2) {
     *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(num[0] * inv, num[1] * inv);
   } else {
     out[0] = static_cast<bf16>(num[0] * inv);
   }
   if (p.lse != nullptr && lane == 0)
-    p.lse[(size_t)b * p.Hq + h] = n > 0 ? (M + __log2f(den)) * kLn2 : kNegInf;
+    p.lse[(size_t)b * p.Hq + h] = (M + __log2f(den)) * kLn2;
 }
 
 int max_splits(int max_blocks, int block_size) {

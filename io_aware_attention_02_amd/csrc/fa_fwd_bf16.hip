@@ -56,12 +56,7 @@ constexpr int kWQ = 32;                // query rows per wave
 constexpr int kBM = kNW * kWQ;         // query rows per workgroup
 constexpr int kBN = 64;                // keys per tile
 constexpr int kThreads = 64 * kNW;
-constexpr float kTau = 8.f;            // lazy-rescale threshold (log2 units)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
-#ifndef FA_FWD_PIPE
-#define FA_FWD_PIPE 0
-#endif
-constexpr bool kPipe = FA_FWD_PIPE;    // software-pipelined variant (see the loop below)
 
 template <int D>
 struct Geo {
@@ -113,9 +108,14 @@ __device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0
                                           const int (&off)[Geo<D>::NI_W], int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists only for the GPU target
   using G = Geo<D>;
-  const int bytes = max(L - key0, 0) * G::RB;
+  // The tile's base and size are the same for every lane; readfirstlane states it so the
+  // resource stays in scalar registers.
+  const int bytes = __builtin_amdgcn_readfirstlane(max(L - key0, 0) * G::RB);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(head + (size_t)key0 * D);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(head + (size_t)key0 * D), (short)0, bytes, kBufferFlags);
+      reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
 #pragma unroll
   for (int t = 0; t < G::NI_W; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * G::NI_W + t) * 1024, 16, off[t],
@@ -154,6 +154,8 @@ __device__ __forceinline__ FragAddr<D> frag_addr(int lane) {
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002;
+constexpr int kValuPerMfma = 8;  // vector instructions placed after each P V MFMA
 
 // S^T (64 keys x 32 queries of this wave) = K_tile Q^T: 2*D/16 fragment reads and MFMAs.  The
 // reads run kAheadK fragments ahead of the MFMAs that consume them, which hides the LDS
@@ -165,6 +167,7 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const lds_t* Kb, const Fr
   using G = Geo<D>;
   constexpr int NM = 2 * G::KC;
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
   s[0] = f32x16{};
   s[1] = f32x16{};
 #pragma unroll
@@ -183,37 +186,7 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const lds_t* Kb, const Fr
   }
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadK, 0);
   __builtin_amdgcn_sched_barrier(0);
-}
-
-// O^T (d x 32 queries) += V_tile^T P^T: 4*D/32 MFMAs, each fed by two transposing reads, which
-// run kAheadV MFMAs ahead.
-constexpr int kAheadV = 4;
-template <int D>
-__device__ __forceinline__ void pv(f32x16 (&acc)[D / 32], const lds_t* Vb, const FragAddr<D>& fa,
-                                   const bf16x8 (&pf)[4]) {
-  using G = Geo<D>;
-  constexpr int NM = 4 * G::NB;
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-    for (int n = 0; n < G::NB; ++n) {
-      const lds_t* p = Vb + fa.v[n] + jj * 16 * G::RB;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * G::RB));
-      const bf16x8 vf = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[n] = mfma32(vf, pf[jj], acc[n]);
-    }
-  }
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAheadV, 0);
-#pragma unroll
-  for (int i = 0; i < NM - kAheadV; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadV, 0);
-  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Masks the scores a query row may not see: keys at or past L, and (causal) keys after it.
@@ -239,34 +212,71 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   return max_xor32(fmaxf(m0, m1));
 }
 
-// Probabilities of one tile, exp2(s * sl2 - m), packed to bf16 in the k-slot order of the
-// P^T operand; returns their sum over this lane's 32 keys.  On masked tiles a masked score
+// Probabilities of one 16-key chunk (jj) of the tile: exp2(s * sl2 - m), packed to bf16 in the
+// k-slot order of the P^T operand; their sum is added to rs.  On masked tiles a masked score
 // (-inf) gives exactly 0 even when the scale is 0 (where -inf * 0 would be NaN).
 template <bool MASKED>
-__device__ __forceinline__ float probs(bf16x8 (&pf)[4], const f32x16 (&s)[2], float sl2,
-                                       float m_use) {
-  float rs0 = 0.f, rs1 = 0.f;
+__device__ __forceinline__ bf16x8 chunk_probs(const f32x16 (&s)[2], int jj, float sl2, float m_use,
+                                              float& rs) {
+  float e[8];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    float e[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float x = s[jj >> 1][8 * (jj & 1) + t];
-      float arg = fmaf(x, sl2, -m_use);
-      if (MASKED && x == kNegInf) arg = kNegInf;
-      e[t] = fast_exp2(arg);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      rs0 += e[t];
-      rs1 += e[t + 1];
-    }
-    pf[jj] = pack_bf16x8(e);
+  for (int t = 0; t < 8; ++t) {
+    const float x = s[jj >> 1][8 * (jj & 1) + t];
+    float arg = fmaf(x, sl2, -m_use);
+    if (MASKED && x == kNegInf) arg = kNegInf;
+    e[t] = fast_exp2(arg);
   }
-  return rs0 + rs1;
+  rs += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  return pack_bf16x8(e);
 }
 
-template <int D, bool CAUSAL, bool PIPE>
+// Softmax and O^T (d x 32 queries) = alpha O^T + V_tile^T P^T, interleaved.  The MFMAs run
+// chunk by chunk (16 keys) over the D/32 output blocks, each fed by two transposing V reads
+// kAheadV MFMAs ahead.  While they run, the vector ALU rescales the output blocks not yet
+// touched (alpha) and computes the next chunk's probabilities, so most of the softmax hides
+// under the matrix work.  Returns this lane's part of the tile's row sum.
+constexpr int kAheadV = 4;
+template <int D, bool MASKED>
+__device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* Vb,
+                                            const FragAddr<D>& fa, const f32x16 (&s)[2],
+                                            float sl2, float m_use, float alpha) {
+  using G = Geo<D>;
+  constexpr int NM = 4 * G::NB;
+  float rs = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 pf[4];
+  pf[0] = chunk_probs<MASKED>(s, 0, sl2, m_use, rs);
+  acc[0] *= alpha;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+      const lds_t* p = Vb + fa.v[n] + jj * 16 * G::RB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * G::RB));
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (jj == 0 && n + 1 < G::NB) acc[n + 1] *= alpha;
+      acc[n] = mfma32(vf, pf[jj], acc[n]);
+    }
+    if (jj + 1 < 4) pf[jj + 1] = chunk_probs<MASKED>(s, jj + 1, sl2, m_use, rs);
+  }
+  // Schedule: the first reads, then per MFMA a few vector instructions and the next reads.
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAheadV, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+    if (i + kAheadV < NM) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  return rs;
+}
+
+template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(Params p) {
   using G = Geo<D>;
@@ -320,10 +330,9 @@ fwd_bf16_kernel(Params p) {
   tile_offsets<D, false>(koff, wave, lane);
   tile_offsets<D, true>(voff, wave, lane);
 
-  // Issue the first loads before anything else: K_0, V_0 (and K_1 when pipelined).
+  // Issue the first loads before anything else: K_0 and V_0.
   load_tile<D>(K0, Kg, 0, L, koff, wave);
   load_tile<D>(V0, Vg, 0, L, voff, wave);
-  if (PIPE && n_kt > 1) load_tile<D>(K1, Kg, kBN, L, koff, wave);
 
   // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel.
   bf16x8 qf[G::KC];
@@ -340,102 +349,59 @@ fwd_bf16_kernel(Params p) {
   float m_run = kNegInf;  // reference maximum (log2 units); -inf until a key is seen
   float l_run = 0.f;      // this lane's share of the row sum (relative to m_run)
 
-  f32x16 sA[2], sB[2];
+  f32x16 sA[2];
   wait_loads();
   __syncthreads();
 
-  // Row statistics of a fresh score tile: mask (only on tiles that need it), row maximum and
-  // the lazy rescale.  The rescale branch is wave-uniform and rare.
-  auto row_max = [&](f32x16 (&s)[2], int key0, auto masked) {
-    if constexpr (decltype(masked)::value) mask_scores<CAUSAL>(s, key0, L, qrow, hh);
-    const float mx = tile_max(s);
-    return (mx == kNegInf) ? kNegInf : mx * sl2;
-  };
-  auto rescale = [&](float mt) {
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
-      m_run = m_new;
-    }
-  };
-  auto needs_mask = [&](int key0) {
-    return (key0 + kBN > L) || (CAUSAL && key0 + kBN - 1 > qw0);
+  // One tile: S = Q K^T, row maxima (masked only where some key must be hidden), the new
+  // running maximum and the rescale factor alpha (1 when the maximum did not grow), then the
+  // probabilities and O = alpha O + V P.
+  auto tile = [&](const lds_t* Kc, const lds_t* Vc, int key0, auto masked) __attribute__((always_inline)) {
+    constexpr bool M = decltype(masked)::value;
+    scores<D>(sA, Kc, fa, qf);
+    if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
+    const float mx = tile_max(sA);
+    const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // -inf only before any visible key
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run = fmaf(alpha, l_run, softmax_pv<D, M>(acc, Vc, fa, sA, sl2, m_use, alpha));
   };
 
-  if constexpr (PIPE) {
-    scores<D>(sA, K0, fa, qf);
-    rescale(needs_mask(0) ? row_max(sA, 0, std::true_type{}) : row_max(sA, 0, std::false_type{}));
-
-    // Iteration j: S_{j+1} = Q K_{j+1}^T and P_j = exp2(S_j - m); then O += V_j P_j and the
-    // row maxima of S_{j+1}; V_{j+1} and K_{j+2} load meanwhile.  With no branch between them,
-    // the matrix instructions of one part and the vector instructions of the other are
-    // scheduled together.  Buffers alternate, so the body is instantiated for even and odd j,
-    // keeping every LDS access on a fixed buffer.
-    auto body = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], lds_t* Kn, lds_t* Vc, lds_t* Vn,
-                    lds_t* Kf) {
-      if (j + 1 < n_kt) load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
-      if (j + 2 < n_kt) load_tile<D>(Kf, Kg, (j + 2) * kBN, L, koff, wave);
-      const float m_use = m_run == kNegInf ? 0.f : m_run;
-      if (j + 1 < n_kw) {
-        const int key1 = (j + 1) * kBN;
-        float mt;
-        bf16x8 pf[4];
-        if (needs_mask(key1)) {
-          scores<D>(sn, Kn, fa, qf);
-          l_run += probs<true>(pf, sc, sl2, m_use);
-          pv<D>(acc, Vc, fa, pf);
-          mt = row_max(sn, key1, std::true_type{});
-        } else {
-          scores<D>(sn, Kn, fa, qf);
-          l_run += probs<true>(pf, sc, sl2, m_use);
-          pv<D>(acc, Vc, fa, pf);
-          mt = row_max(sn, key1, std::false_type{});
-        }
-        rescale(mt);
-      } else if (j < n_kw) {
-        bf16x8 pf[4];
-        l_run += probs<true>(pf, sc, sl2, m_use);
-        pv<D>(acc, Vc, fa, pf);
-      }
-      wait_loads();
-      __syncthreads();
-    };
-    for (int j = 0; j < n_kt; j += 2) {
-      body(j, sA, sB, K1, V0, V1, K0);
-      if (j + 1 < n_kt) body(j + 1, sB, sA, K0, V1, V0, K1);
+  // Iteration j computes tile j from buffers j % 2 while tile j+1 loads into the others.  The
+  // buffer is fixed per instantiation, so every LDS access refers to one known buffer and the
+  // compiler never waits for the loads in flight.  Tiles [0, n_main) need no mask for any wave
+  // of the workgroup; the remaining ones (the causal diagonal, the ragged end) are masked.
+  const int n_main = CAUSAL ? min(q0, L) / kBN : L / kBN;
+  auto iter = [&](int j, auto parity, auto masked) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(parity)::value;
+    lds_t* const Kc = ODD ? K1 : K0;
+    lds_t* const Vc = ODD ? V1 : V0;
+    lds_t* const Kn = ODD ? K0 : K1;
+    lds_t* const Vn = ODD ? V0 : V1;
+    if (j + 1 < n_kt) {
+      load_tile<D>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
+      load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
     }
-  } else {
-    // Iteration j: S_j = Q K_j^T, row maxima, P_j, O += V_j P_j, while K_{j+1} and V_{j+1}
-    // load into the other buffers.  The overlap of matrix and vector work comes from the
-    // second workgroup on each SIMD.
-    auto body = [&](int j, lds_t* Kc, lds_t* Vc, lds_t* Kn, lds_t* Vn) {
-      if (j + 1 < n_kt) {
-        load_tile<D>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
-        load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
-      }
-      if (j < n_kw) {
-        const int key0 = j * kBN;
-        auto tile = [&](auto masked) {
-          constexpr bool M = decltype(masked)::value;
-          scores<D>(sA, Kc, fa, qf);
-          rescale(row_max(sA, key0, masked));
-          bf16x8 pf[4];
-          l_run += probs<M>(pf, sA, sl2, m_run == kNegInf ? 0.f : m_run);
-          pv<D>(acc, Vc, fa, pf);
-        };
-        if (needs_mask(key0)) tile(std::true_type{});
-        else tile(std::false_type{});
-      }
-      wait_loads();
-      __syncthreads();
-    };
-    for (int j = 0; j < n_kt; j += 2) {
-      body(j, K0, V0, K1, V1);
-      if (j + 1 < n_kt) body(j + 1, K1, V1, K0, V0);
-    }
+    if (j < n_kw) tile(Kc, Vc, j * kBN, masked);
+    wait_loads();
+    __syncthreads();
+  };
+  using even = std::false_type;
+  using odd = std::true_type;
+  int j = 0;
+  for (; j + 1 < n_main; j += 2) {
+    iter(j, even{}, std::false_type{});
+    iter(j + 1, odd{}, std::false_type{});
+  }
+  if (j < n_main) {
+    iter(j, even{}, std::false_type{});
+    ++j;
+  }
+  for (; j < n_kt; ++j) {
+    if (j & 1) iter(j, odd{}, std::true_type{});
+    else iter(j, even{}, std::true_type{});
   }
 
   // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
@@ -457,7 +423,7 @@ fwd_bf16_kernel(Params p) {
   }
 }
 
-template <int D, bool CAUSAL, bool PIPE = kPipe>
+template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   Params p;
   p.q = static_cast<const bf16*>(a.q);
@@ -473,7 +439,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.n_qt = (a.N + kBM - 1) / kBM;
   p.total = a.B * a.H * p.n_qt;
   p.sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PIPE>), dim3(p.total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
