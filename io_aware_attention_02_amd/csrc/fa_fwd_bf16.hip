@@ -56,6 +56,7 @@ constexpr int kWQ = 32;                // query rows per wave
 constexpr int kBM = kNW * kWQ;         // query rows per workgroup
 constexpr int kBN = 64;                // keys per tile
 constexpr int kThreads = 64 * kNW;
+constexpr float kTau = 16.f;           // headroom of the fixed reference (log2 units)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
 
 template <int D>
@@ -236,7 +237,7 @@ __device__ __forceinline__ bf16x8 chunk_probs(const f32x16 (&s)[2], int jj, floa
 // touched (alpha) and computes the next chunk's probabilities, so most of the softmax hides
 // under the matrix work.  Returns this lane's part of the tile's row sum.
 constexpr int kAheadV = 4;
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool RESCALE>
 __device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* Vb,
                                             const FragAddr<D>& fa, const f32x16 (&s)[2],
                                             float sl2, float m_use, float alpha) {
@@ -246,7 +247,7 @@ __device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* 
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 pf[4];
   pf[0] = chunk_probs<MASKED>(s, 0, sl2, m_use, rs);
-  acc[0] *= alpha;
+  if (RESCALE) acc[0] *= alpha;
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -258,7 +259,7 @@ __device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* 
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * G::RB));
       const bf16x8 vf = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      if (jj == 0 && n + 1 < G::NB) acc[n + 1] *= alpha;
+      if (RESCALE && jj == 0 && n + 1 < G::NB) acc[n + 1] *= alpha;
       acc[n] = mfma32(vf, pf[jj], acc[n]);
     }
     if (jj + 1 < 4) pf[jj + 1] = chunk_probs<MASKED>(s, jj + 1, sl2, m_use, rs);
@@ -350,23 +351,35 @@ fwd_bf16_kernel(Params p) {
   float l_run = 0.f;      // this lane's share of the row sum (relative to m_run)
 
   f32x16 sA[2];
-  wait_loads();
-  __syncthreads();
 
-  // One tile: S = Q K^T, row maxima (masked only where some key must be hidden), the new
-  // running maximum and the rescale factor alpha (1 when the maximum did not grow), then the
-  // probabilities and O = alpha O + V P.
-  auto tile = [&](const lds_t* Kc, const lds_t* Vc, int key0, auto masked) __attribute__((always_inline)) {
+  // The K/V loop runs in one of two modes.
+  //  * FAST (first try): every row keeps the maximum of its first tile as a fixed reference, so
+  //    nothing accumulated is ever rescaled; a later row maximum above the reference by more than
+  //    kTau only raises a flag (probabilities stay below 2^kTau, far inside bf16/fp32 range).
+  //  * SAFE: the running maximum with a rescale of O and l whenever it grows
+  //    ("FlashAttention优化" §3.2.1), taken only if some wave of the workgroup raised the flag.
+  // With a fixed reference the output and the row sum are the same sums the recurrence forms, so
+  // both modes give the exact softmax.
+  enum { FIRST = 0, FAST = 1, SAFE = 2 };
+  bool flagged = false;
+  auto tile = [&](const lds_t* Kc, const lds_t* Vc, int key0, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool M = decltype(masked)::value;
+    constexpr int MODE = decltype(mode)::value;
     scores<D>(sA, Kc, fa, qf);
     if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
     const float mx = tile_max(sA);
     const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // -inf only before any visible key
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run = fmaf(alpha, l_run, softmax_pv<D, M>(acc, Vc, fa, sA, sl2, m_use, alpha));
+    if constexpr (MODE == SAFE) {
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // -inf only before any visible key
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      l_run = fmaf(alpha, l_run, softmax_pv<D, M, true>(acc, Vc, fa, sA, sl2, m_use, alpha));
+    } else {
+      if constexpr (MODE == FIRST) m_run = (mt == kNegInf) ? 0.f : mt;
+      else flagged |= mt > m_run + kTau;
+      l_run += softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
+    }
   };
 
   // Iteration j computes tile j from buffers j % 2 while tile j+1 loads into the others.  The
@@ -374,7 +387,7 @@ fwd_bf16_kernel(Params p) {
   // compiler never waits for the loads in flight.  Tiles [0, n_main) need no mask for any wave
   // of the workgroup; the remaining ones (the causal diagonal, the ragged end) are masked.
   const int n_main = CAUSAL ? min(q0, L) / kBN : L / kBN;
-  auto iter = [&](int j, auto parity, auto masked) __attribute__((always_inline)) {
+  auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(parity)::value;
     lds_t* const Kc = ODD ? K1 : K0;
     lds_t* const Vc = ODD ? V1 : V0;
@@ -384,24 +397,45 @@ fwd_bf16_kernel(Params p) {
       load_tile<D>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
       load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
     }
-    if (j < n_kw) tile(Kc, Vc, j * kBN, masked);
+    if (j < n_kw) tile(Kc, Vc, j * kBN, masked, mode);
     wait_loads();
     __syncthreads();
   };
   using even = std::false_type;
   using odd = std::true_type;
-  int j = 0;
-  for (; j + 1 < n_main; j += 2) {
-    iter(j, even{}, std::false_type{});
-    iter(j + 1, odd{}, std::false_type{});
-  }
-  if (j < n_main) {
-    iter(j, even{}, std::false_type{});
-    ++j;
-  }
-  for (; j < n_kt; ++j) {
-    if (j & 1) iter(j, odd{}, std::true_type{});
-    else iter(j, even{}, std::true_type{});
+  using unmasked = std::false_type;
+  using masked = std::true_type;
+  auto run = [&](auto mode) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
+    using first_mode = std::integral_constant<int, MODE == SAFE ? SAFE : FIRST>;
+    // Tile 0 (K_0 and V_0 are loading or loaded): the FAST pass takes its references from it.
+    wait_loads();
+    __syncthreads();
+    if (0 < n_main) iter(0, even{}, unmasked{}, first_mode{});
+    else iter(0, even{}, masked{}, first_mode{});
+    int j = 1;
+    for (; j + 1 < n_main; j += 2) {
+      iter(j, odd{}, unmasked{}, mode);
+      iter(j + 1, even{}, unmasked{}, mode);
+    }
+    if (j < n_main) {
+      iter(j, odd{}, unmasked{}, mode);
+      ++j;
+    }
+    for (; j < n_kt; ++j) {
+      if (j & 1) iter(j, odd{}, masked{}, mode);
+      else iter(j, even{}, masked{}, mode);
+    }
+  };
+  run(std::integral_constant<int, FAST>{});
+  if (__syncthreads_or(flagged)) {  // some row's maximum outgrew its reference: exact fallback
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
+    m_run = kNegInf;
+    l_run = 0.f;
+    load_tile<D>(K0, Kg, 0, L, koff, wave);
+    load_tile<D>(V0, Vg, 0, L, voff, wave);
+    run(std::integral_constant<int, SAFE>{});
   }
 
   // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).

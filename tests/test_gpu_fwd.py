@@ -130,6 +130,20 @@ def test_scale_zero_and_custom_scale():
             _check(q, k, v, o, lse, causal, None, scale, TOL_O_BF16)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_maximum_far_above_first_tile(causal):
+    # One key of a later tile scores ~50 log2-units above every key of the first tile for every
+    # query row (positive queries, a key of all 4s).  A pass that keeps the first tile's maximum
+    # as the reference must notice and redo the rows exactly with the rescaling recurrence.
+    say(f"fa_fwd row maximum far above the first tile causal={causal}")
+    B, H, Hkv, N, d = 1, 2, 1, 1000, 128
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=12)
+    q = q.abs()
+    k[:, :, 500] = 4.0
+    o, lse = _run(q, k, v, causal)
+    _check(q, k, v, o, lse, causal, None, 1 / d ** 0.5, TOL_O_BF16)
+
+
 def test_gqa_equals_repeated_kv_bitwise():
     say("fa_fwd GQA vs repeated-KV MHA")
     B, H, Hkv, N, d = 2, 8, 2, 333, 128
