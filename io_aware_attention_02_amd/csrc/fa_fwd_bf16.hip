@@ -51,11 +51,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-constexpr int kNW = 4;                 // waves per workgroup
 constexpr int kWQ = 32;                // query rows per wave
-constexpr int kBM = kNW * kWQ;         // query rows per workgroup
 constexpr int kBN = 64;                // keys per tile
-constexpr int kThreads = 64 * kNW;
+constexpr int kCUs = 256;              // compute units of an MI355X
 constexpr float kTau = 16.f;           // headroom of the fixed reference (log2 units)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
 
@@ -65,16 +63,21 @@ struct Geo {
   static constexpr int CPR = RB / 16;              // 16-byte chunks per row
   static constexpr int TILE = kBN * RB;            // bytes per K or V tile
   static constexpr int NI = TILE / 1024;           // 1 KB direct loads per tile
-  static constexpr int NI_W = NI / kNW;            // ... per wave
   static constexpr int RPI = 1024 / RB;            // rows per direct load
   static constexpr int KC = D / 16;                // 16-dim steps of the score contraction
   static constexpr int NB = D / 32;                // 32-dim blocks of the output
-  static_assert(NI % kNW == 0, "tile loads split evenly over the waves");
   // Chunk swizzles (XOR on the 16-byte chunk index of a row).  K: 16 consecutive rows read at
   // one logical chunk hit 16 distinct bank groups.  V: the 8 rows x 64 bytes that one
   // transposing read touches cover every bank group exactly twice.
   __device__ static int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
   __device__ static int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+};
+
+// Direct tile loads per wave for a workgroup of NW waves.
+template <int D, int NW>
+struct LoadGeo {
+  static constexpr int NI_W = Geo<D>::NI / NW;
+  static_assert(Geo<D>::NI % NW == 0, "tile loads split evenly over the waves");
 };
 
 struct Params {
@@ -89,12 +92,13 @@ struct Params {
 };
 
 // Per-lane byte offsets of this wave's direct loads inside a tile (row * RB + swizzled chunk).
-template <int D, bool IS_V>
-__device__ __forceinline__ void tile_offsets(int (&off)[Geo<D>::NI_W], int wave, int lane) {
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void tile_offsets(int* off, int wave, int lane) {
   using G = Geo<D>;
+  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
 #pragma unroll
-  for (int t = 0; t < G::NI_W; ++t) {
-    const int row = (wave * G::NI_W + t) * G::RPI + lane / G::CPR;
+  for (int t = 0; t < NI_W; ++t) {
+    const int row = (wave * NI_W + t) * G::RPI + lane / G::CPR;
     const int chunk = (lane % G::CPR) ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
     off[t] = row * G::RB + chunk * 16;
   }
@@ -104,11 +108,12 @@ __device__ __forceinline__ void tile_offsets(int (&off)[Geo<D>::NI_W], int wave,
 // resource whose base is the tile's first row and whose size ends at the valid length L: rows
 // at or past L are out of range and arrive as zeros (their scores are masked, so they add
 // exactly nothing), and no load can leave the tensor.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0, int L,
-                                          const int (&off)[Geo<D>::NI_W], int wave) {
+                                          const int* off, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists only for the GPU target
   using G = Geo<D>;
+  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
   // The tile's base and size are the same for every lane; readfirstlane states it so the
   // resource stays in scalar registers.
   const int bytes = __builtin_amdgcn_readfirstlane(max(L - key0, 0) * G::RB);
@@ -118,8 +123,8 @@ __device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
 #pragma unroll
-  for (int t = 0; t < G::NI_W; ++t)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * G::NI_W + t) * 1024, 16, off[t],
+  for (int t = 0; t < NI_W; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * NI_W + t) * 1024, 16, off[t],
                                              0, 0, 0);
 #endif
 }
@@ -277,10 +282,13 @@ __device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* 
   return rs;
 }
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(Params p) {
   using G = Geo<D>;
+  constexpr int kBM = NW * kWQ;         // query rows per workgroup
+  constexpr int kThreads = 64 * NW;
+  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
   __shared__ __attribute__((aligned(1024))) char k0s[G::TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[G::TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[G::TILE];
@@ -327,13 +335,13 @@ fwd_bf16_kernel(Params p) {
   // Tiles this wave needs (fewer than n_kt on the causal diagonal).
   const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
   const float sl2 = p.sl2;
-  int koff[G::NI_W], voff[G::NI_W];
-  tile_offsets<D, false>(koff, wave, lane);
-  tile_offsets<D, true>(voff, wave, lane);
+  int koff[NI_W], voff[NI_W];
+  tile_offsets<D, NW, false>(koff, wave, lane);
+  tile_offsets<D, NW, true>(voff, wave, lane);
 
   // Issue the first loads before anything else: K_0 and V_0.
-  load_tile<D>(K0, Kg, 0, L, koff, wave);
-  load_tile<D>(V0, Vg, 0, L, voff, wave);
+  load_tile<D, NW>(K0, Kg, 0, L, koff, wave);
+  load_tile<D, NW>(V0, Vg, 0, L, voff, wave);
 
   // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel.
   bf16x8 qf[G::KC];
@@ -394,8 +402,8 @@ fwd_bf16_kernel(Params p) {
     lds_t* const Kn = ODD ? K0 : K1;
     lds_t* const Vn = ODD ? V0 : V1;
     if (j + 1 < n_kt) {
-      load_tile<D>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
-      load_tile<D>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
+      load_tile<D, NW>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
+      load_tile<D, NW>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
     }
     if (j < n_kw) tile(Kc, Vc, j * kBN, masked, mode);
     wait_loads();
@@ -433,8 +441,8 @@ fwd_bf16_kernel(Params p) {
     for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
     m_run = kNegInf;
     l_run = 0.f;
-    load_tile<D>(K0, Kg, 0, L, koff, wave);
-    load_tile<D>(V0, Vg, 0, L, voff, wave);
+    load_tile<D, NW>(K0, Kg, 0, L, koff, wave);
+    load_tile<D, NW>(V0, Vg, 0, L, voff, wave);
     run(std::integral_constant<int, SAFE>{});
   }
 
@@ -470,10 +478,19 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.group = a.H / a.Hkv;
   p.Hkv = a.Hkv;
   p.N = a.N;
-  p.n_qt = (a.N + kBM - 1) / kBM;
-  p.total = a.B * a.H * p.n_qt;
   p.sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
+  // Eight waves (256 rows) per workgroup share each K/V tile in LDS when that still gives every
+  // CU a workgroup; otherwise four waves (128 rows), two workgroups per CU.
+  const long long wide = (long long)a.B * a.H * ((a.N + 8 * kWQ - 1) / (8 * kWQ));
+  if (wide >= kCUs) {
+    p.n_qt = (a.N + 8 * kWQ - 1) / (8 * kWQ);
+    p.total = a.B * a.H * p.n_qt;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+  } else {
+    p.n_qt = (a.N + 4 * kWQ - 1) / (4 * kWQ);
+    p.total = a.B * a.H * p.n_qt;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3(p.total), dim3(64 * 4), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

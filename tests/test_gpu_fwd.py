@@ -144,6 +144,36 @@ def test_row_maximum_far_above_first_tile(causal):
     _check(q, k, v, o, lse, causal, None, 1 / d ** 0.5, TOL_O_BF16)
 
 
+# Grids with at least one 256-row workgroup per CU run the eight-wave kernel; these shapes
+# reach it with ragged lengths, grouped heads, padding and the fallback pass.
+WIDE = [
+    # (B, H, Hkv, N, d, causal, lens)
+    (2, 32, 8, 1000, 128, True, [1000, 517]),
+    (2, 32, 32, 777, 128, False, [777, 1]),
+    (4, 16, 4, 1025, 64, True, [1025, 300, 0, 256]),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=[f"B{s[0]}H{s[1]}Hkv{s[2]}N{s[3]}d{s[4]}{'c' if s[5] else ''}" for s in WIDE])
+def test_wide_grid_shapes(shape):
+    B, H, Hkv, N, d, causal, lens = shape
+    say(f"fa_fwd wide grid {shape}")
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=13 + N)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    o, lse = _run(q, k, v, causal, sl)
+    _check(q, k, v, o, lse, causal, sl, 1 / d ** 0.5, TOL_O_BF16)
+
+
+def test_wide_grid_row_maximum_far_above_first_tile():
+    say("fa_fwd wide grid, row maximum far above the first tile")
+    B, H, Hkv, N, d = 2, 32, 8, 1000, 128
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=14)
+    q = q.abs()
+    k[:, :, 700] = 4.0
+    o, lse = _run(q, k, v, True)
+    _check(q, k, v, o, lse, True, None, 1 / d ** 0.5, TOL_O_BF16)
+
+
 def test_gqa_equals_repeated_kv_bitwise():
     say("fa_fwd GQA vs repeated-KV MHA")
     B, H, Hkv, N, d = 2, 8, 2, 333, 128
