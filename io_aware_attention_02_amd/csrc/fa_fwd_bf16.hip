@@ -54,6 +54,7 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 constexpr int kWQ = 32;                // query rows per wave
 constexpr int kBN = 64;                // keys per tile
 constexpr int kCUs = 256;              // compute units of an MI355X
+constexpr int kXcds = 8;               // accelerator complex dies (each with its own L2)
 constexpr float kTau = 16.f;           // headroom of the fixed reference (log2 units)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
 
@@ -302,13 +303,23 @@ fwd_bf16_kernel(Params p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, hh = lane >> 5;
 
+  // Work unit = (batch, kv head): the group's query heads and their query tiles, which all read
+  // the same K/V.  Each XCD runs a contiguous range of logical tiles (shared L2); when the units
+  // divide evenly, XCD x takes units x, x+8, x+16, ... so every XCD holds the same mix of
+  // sequences (causal work grows with the square of a sequence's length).
   const int lam = xcd_remap(blockIdx.x, p.total);
-  const int bh = lam / p.n_qt;
-  int qt = lam - bh * p.n_qt;
+  const int per_unit = p.group * p.n_qt;
+  const int units = p.total / per_unit;
+  int unit = lam / per_unit;
+  const int rem = lam - unit * per_unit;
+  if (units % kXcds == 0) unit = (unit % (units / kXcds)) * kXcds + unit / (units / kXcds);
+  const int b = unit / p.Hkv, g = unit - b * p.Hkv;
+  const int hi = rem / p.n_qt;
+  int qt = rem - hi * p.n_qt;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
   const int H = p.H, N = p.N;
-  const int b = bh / H, h = bh - b * H;
-  const int g = h / p.group;
+  const int h = g * p.group + hi;
+  const int bh = b * H + h;
   int L = N;
   if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
 
