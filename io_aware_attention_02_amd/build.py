@@ -55,6 +55,8 @@ def _compile(src, hipcc, verbose):
 def build_library(verbose=False):
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
+    if os.path.exists(OUT):  # a failed build must not leave an older library behind
+        os.remove(OUT)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, hipcc, verbose), srcs))

@@ -96,11 +96,13 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (block_size != 16) return FA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
-  // Grid: (Hkv, key-range splits, sequences); the last two dimensions are limited to 65535.
+  // Grid: one 64-thread workgroup per (kv head, key range of 512 tokens, sequence), rounded up
+  // to a multiple of 8 ranges; the total thread count must fit a 32-bit grid.
   const long long splits =
       ((long long)max_blocks_per_seq * block_size + fa::kDecodeSplitTokens - 1) /
       fa::kDecodeSplitTokens;
-  if (splits > 65535 || num_seqs > 65535) return FA_ERR_UNSUPPORTED;
+  const long long units = ((long long)num_seqs * splits + 7) / 8 * 8;
+  if (units * Hkv * 64 > INT_MAX) return FA_ERR_UNSUPPORTED;
   const size_t need =
       fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);
   if (workspace_bytes < need) return FA_ERR_INVALID_ARG;

@@ -21,9 +21,8 @@
 //    (unused columns are zero).  Scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16; P^T is the
 //    score accumulator packed to bf16, the B operand of O^T += V^T P^T
 //    (v_mfma_f32_16x16x16_bf16), so probabilities never leave registers.
-//  * K needs no on-chip staging: each lane loads its A-operand fragment (one token row, a
-//    quarter of the head dimension, 16-byte loads) straight into registers.  The head
-//    dimension is contracted in a permuted order that the query fragments share.
+//  * K needs no on-chip staging: each lane loads its A-operand fragment (one token row, 8 head
+//    dims per MFMA step, 16-byte loads) straight into registers.
 //  * V goes from global memory straight into LDS (buffer_load ... lds, 16 bytes per lane,
 //    chunks XOR-swizzled by row) and its V^T fragments are read with ds_read_b64_tr_b16.
 //  * Every load is issued kStages-1 blocks ahead of its use through a per-block buffer
@@ -44,6 +43,7 @@ constexpr int kSplit = kDecodeSplitTokens;      // tokens per wave
 constexpr int kBlocksPerSplit = kSplit / kBS;   // block ids prefetched per wave (<= 64)
 constexpr int kStages = 4;                      // blocks in the load ring
 constexpr int kBufferFlags = 0x00020000;        // buffer resource word 3: 32-bit data, raw
+constexpr int kXcds = 8;                        // accelerator complex dies (each with its own L2)
 static_assert(kBlocksPerSplit <= 64, "one block id per lane");
 
 struct DecodeParams {
@@ -57,7 +57,7 @@ struct DecodeParams {
   float* opart;  // [S][Hq][MS][D]
   float* mpart;  // [S][Hq][MS]
   float* lpart;  // [S][Hq][MS]
-  int Hq, Hkv, group, max_blocks, max_tokens, MS;
+  int Hq, Hkv, group, max_blocks, max_tokens, MS, units;
   float sl2;
 };
 
@@ -70,7 +70,6 @@ struct DGeo {
   static constexpr int RPI = 1024 / RB;         // rows per direct load
   static constexpr int KC = D / 32;             // 16x16x32 MFMAs of the score contraction
   static constexpr int NB = D / 16;             // 16-dim output blocks
-  static constexpr int QD = D / 4;              // head dims held by one lane group
   // V chunk swizzle: the 16 rows x 32 bytes of one transposing read hit every bank group
   // exactly twice.
   __device__ static int swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
@@ -107,7 +106,7 @@ __device__ __forceinline__ void issue_block(KFrag<D>& kf, lds_t* vs, const Block
 #pragma unroll
   for (int c = 0; c < G::KC; ++c)
     kf.c[c] = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k, koff + 16 * c, 0, 0));
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k, koff + 64 * c, 0, 0));
 #pragma unroll
   for (int t = 0; t < G::NDMA; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, vs + t * 1024, 16, voff[t], 0, 0, 0);
@@ -132,7 +131,15 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
   constexpr int kLoadsPerBlock = G::KC + G::NDMA;
 
   const int lane = threadIdx.x;
-  const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Work unit u = one key range
+  // of one sequence (b * MS + sp); its Hkv waves (one per kv head) take consecutive slots of one
+  // XCD, so that XCD streams whole physical blocks ([16][Hkv][d] contiguous) while units go
+  // round-robin over the XCDs (every XCD gets a share of every sequence).
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int g = slot % p.Hkv;
+  const int u = (slot / p.Hkv) * kXcds + xcd;
+  if (u >= p.units) return;
+  const int b = u / p.MS, sp = u - b * p.MS;
   const int L = min(max(p.lens[b], 0), p.max_tokens);
   const int tok_begin = sp * kSplit;
   if (tok_begin >= L) return;
@@ -145,8 +152,9 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
 
   const int row_bytes = p.Hkv * G::RB;
   const int col = lane & 15, grp = lane >> 4;
-  // K: lane holds token `col`, head dims QD*grp .. +QD-1 (16 bytes per MFMA step).
-  const int koff = col * row_bytes + (g * D + G::QD * grp) * 2;
+  // K: for MFMA step c, lane holds token `col`, head dims 32c + 8*grp .. +7; one load
+  // instruction covers 16 token rows x 64 contiguous bytes.
+  const int koff = col * row_bytes + (g * D + 8 * grp) * 2;
   // V: direct load t writes LDS rows RPI*t .. +RPI-1; lane -> (row, swizzled chunk).
   int voff[G::NDMA];
 #pragma unroll
@@ -175,7 +183,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int c = 0; c < G::KC; ++c) {
     qf[c] = head_ok
-                ? *reinterpret_cast<const bf16x8*>(p.q + ((size_t)b * p.Hq + qh) * D + G::QD * grp + 8 * c)
+                ? *reinterpret_cast<const bf16x8*>(p.q + ((size_t)b * p.Hq + qh) * D + 32 * c + 8 * grp)
                 : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
@@ -360,7 +368,9 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.mpart = p.opart + slots * D;
   p.lpart = p.mpart + slots;
   p.sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(a.Hkv, p.MS, a.S), dim3(64), 0, stream, p);
+  p.units = a.S * p.MS;
+  const long long grid_slots = (long long)((p.units + kXcds - 1) / kXcds) * a.Hkv;
+  hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)(grid_slots * kXcds)), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.S), dim3(64), 0, stream, p);

@@ -97,7 +97,7 @@ def _dec(lib, **kw):
     (dict(kc=P + 8), INVALID), (dict(ws=P + 4), INVALID), (dict(bt=P + 2), INVALID),
     (dict(lse=P + 1), INVALID), (dict(wsb=1000), INVALID),
     (dict(d=80), UNSUPPORTED), (dict(bs=32), UNSUPPORTED), (dict(Hq=64, Hkv=2), UNSUPPORTED),
-    (dict(S=70000), UNSUPPORTED),
+    (dict(S=1 << 20, M=1 << 14), UNSUPPORTED),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _dec(lib, **kw) == status
