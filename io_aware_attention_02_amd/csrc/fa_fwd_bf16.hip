@@ -11,33 +11,33 @@
 // it.
 //
 // CDNA4 mapping (the pages' A100/H100 tile sizes are prior art, not used):
-//  * 4 waves x 32 query rows (BM = 128), BN = 64 keys per tile.  A wave holds its Q^T
-//    fragments, two score tiles and the 32 x d output accumulator in registers (<= 256 per
-//    lane), so two workgroups share a CU and the two waves on every SIMD come from different
-//    workgroups: one's softmax (VALU) overlaps the other's matrix work.
+//  * A wave owns 32 query rows; BN = 64 keys per tile.  A workgroup is 8 waves (256 rows, one
+//    workgroup per CU, two waves per SIMD) when that still gives every CU a workgroup, else 4
+//    waves (128 rows, two workgroups per CU).  A wave holds its Q^T fragments, one 64 x 32
+//    score tile and the 32 x d output accumulator in registers (<= 256 per lane).
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows are
 //    the A operand (read from LDS), Q^T the B operand (registers).  The accumulator holds one
-//    query per lane and 16 keys per lane, so the row max/sum are in-lane plus one exchange with
+//    query per lane and 16 keys per lane, so row reductions are in-lane plus one exchange with
 //    lane ^ 32 (v_permlane32_swap).  Packed to bf16, a lane's probabilities are already the B
 //    operand of O^T += V^T P^T (keys in k-slots), so P never leaves registers.
-//  * K and V go from global memory straight into LDS (global_load_lds_dwordx4, no staging
-//    registers), into two buffers each.  The 16-byte chunks of a row are XOR-swizzled by row
-//    so that the fragment reads are free of bank conflicts.  V stays [key][dim] in LDS; its
-//    V^T fragments are read with ds_read_b64_tr_b16, the gfx950 transposing LDS read (each
-//    16-lane group turns a 4-key x 16-dim block into 4 consecutive keys per lane).
-//  * Software pipeline inside a wave: while the matrix cores compute S_{j+1} = Q K_{j+1}^T,
-//    the VALU turns S_j into probabilities; while they compute O += V_j P_j, the VALU takes
-//    the row maxima of S_{j+1}.  The loads of K_{j+2} and V_{j+1} are in flight meanwhile.
-//    One barrier per tile.
-//  * Lazy rescaling: the reference maximum m used in exp2(s - m) only moves when a row's
-//    maximum exceeds it by more than 2^8 (a wave-uniform test).  Probabilities are then at most
-//    256, and since the output and the row sum share the same reference, O = acc / l and
-//    LSE = m + log l are unchanged -- this is the rescale rule of §3.2.1 applied only when it
-//    is needed, not an approximation.
+//  * K and V go from global memory straight into LDS (buffer_load ... lds, no staging
+//    registers), into two buffers each; tile j+1 loads while tile j is computed, one barrier per
+//    tile.  The 16-byte chunks of a row are XOR-swizzled by row so that the fragment reads are
+//    free of bank conflicts.  V stays [key][dim] in LDS; its V^T fragments are read with
+//    ds_read_b64_tr_b16, the gfx950 transposing LDS read (each 16-lane group turns a 4-key x
+//    16-dim block into 4 consecutive keys per lane).
+//  * Inside a tile the score MFMAs run with their fragment reads a few MFMAs ahead; the P V
+//    MFMAs run chunk by chunk (16 keys) with the next chunk's probabilities computed under them.
+//    A wave raises its issue priority while it issues MFMAs, so the matrix cores of a SIMD
+//    switch to the other wave only when this one waits.
+//  * The reference maximum of each row is fixed at its first tile (FAST pass) and checked, not
+//    tracked: no rescaling in the loop.  A later tile whose probabilities could exceed 2^16
+//    raises a flag, and the workgroup then recomputes with the running maximum and rescaling
+//    (SAFE pass).  Both give the exact softmax (details at the K/V loop below).
 //  * The grid is one workgroup per (batch, head, query tile), remapped so that the tiles of one
-//    head (and of one grouped-query kv head) run on the same XCD and share its L2.  Under
-//    causal masking the heaviest query tiles are issued first, tiles past the diagonal are
-//    never loaded, and a wave whose rows all lie above a tile skips its arithmetic.
+//    (batch, kv head) run on the same XCD and share its L2, and so that every XCD gets the same
+//    mix of sequences.  Under causal masking the heaviest query tiles are issued first, tiles
+//    past the diagonal are never loaded, and a wave whose rows all lie above a tile skips it.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -56,6 +56,7 @@ constexpr int kBN = 64;                // keys per tile
 constexpr int kCUs = 256;              // compute units of an MI355X
 constexpr int kXcds = 8;               // accelerator complex dies (each with its own L2)
 constexpr float kTau = 16.f;           // headroom of the fixed reference (log2 units)
+constexpr float kMaxProb = 65536.f;    // 2^kTau
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
 
 template <int D>
@@ -373,8 +374,10 @@ fwd_bf16_kernel(Params p) {
 
   // The K/V loop runs in one of two modes.
   //  * FAST (first try): every row keeps the maximum of its first tile as a fixed reference, so
-  //    nothing accumulated is ever rescaled; a later row maximum above the reference by more than
-  //    kTau only raises a flag (probabilities stay below 2^kTau, far inside bf16/fp32 range).
+  //    nothing accumulated is ever rescaled and later tiles need no maximum at all.  A tile in
+  //    which some lane's share of the row sum exceeds 2^kTau -- the only way one of its
+  //    probabilities can exceed 2^kTau -- raises a flag; otherwise every probability stays far
+  //    inside the bf16/fp32 range.
   //  * SAFE: the running maximum with a rescale of O and l whenever it grows
   //    ("FlashAttention优化" §3.2.1), taken only if some wave of the workgroup raised the flag.
   // With a fixed reference the output and the row sum are the same sums the recurrence forms, so
@@ -386,6 +389,14 @@ fwd_bf16_kernel(Params p) {
     constexpr int MODE = decltype(mode)::value;
     scores<D>(sA, Kc, fa, qf);
     if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
+    if constexpr (MODE == FAST) {
+      // No tile maximum: every probability is at most the lane's share of the tile's row sum,
+      // so that sum exceeding 2^kTau is the test that some score outgrew the reference.
+      const float rs = softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
+      flagged |= rs > kMaxProb;
+      l_run += rs;
+      return;
+    }
     const float mx = tile_max(sA);
     const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
     if constexpr (MODE == SAFE) {
@@ -395,8 +406,7 @@ fwd_bf16_kernel(Params p) {
       m_run = m_new;
       l_run = fmaf(alpha, l_run, softmax_pv<D, M, true>(acc, Vc, fa, sA, sl2, m_use, alpha));
     } else {
-      if constexpr (MODE == FIRST) m_run = (mt == kNegInf) ? 0.f : mt;
-      else flagged |= mt > m_run + kTau;
+      m_run = (mt == kNegInf) ? 0.f : mt;
       l_run += softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
     }
   };
