@@ -21,10 +21,11 @@
 //    (unused columns are zero).  Scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16; P^T is the
 //    score accumulator packed to bf16, the B operand of O^T += V^T P^T
 //    (v_mfma_f32_16x16x16_bf16), so probabilities never leave registers.
-//  * K needs no on-chip staging: each lane loads its A-operand fragment (one token row, 8 head
-//    dims per MFMA step, 16-byte loads) straight into registers.
-//  * V goes from global memory straight into LDS (buffer_load ... lds, 16 bytes per lane,
-//    chunks XOR-swizzled by row) and its V^T fragments are read with ds_read_b64_tr_b16.
+//  * K and V go from global memory straight into LDS (buffer_load ... lds, 16 bytes per lane):
+//    each load instruction covers whole token rows, so it requests whole cache lines.  Chunks are
+//    XOR-swizzled by row so that the fragment reads are free of bank conflicts: K fragments
+//    (one token row, 8 head dims per lane and MFMA step) with ds_read_b128, V^T fragments with
+//    ds_read_b64_tr_b16.
 //  * Every load is issued kStages-1 blocks ahead of its use through a per-block buffer
 //    resource whose size ends at the sequence length: cache slots past the length read as
 //    zeros (never as whatever the pool holds there) and no load leaves the block.
@@ -44,6 +45,9 @@ constexpr int kBlocksPerSplit = kSplit / kBS;   // block ids prefetched per wave
 constexpr int kStages = 4;                      // blocks in the load ring
 constexpr int kBufferFlags = 0x00020000;        // buffer resource word 3: 32-bit data, raw
 constexpr int kXcds = 8;                        // accelerator complex dies (each with its own L2)
+// Cache policy of the K/V loads: nt (non-temporal).  Every cache byte is read exactly once per
+// call, so keeping it in the caches only displaces other lines.
+constexpr int kStreamOnce = 2;
 static_assert(kBlocksPerSplit <= 64, "one block id per lane");
 
 struct DecodeParams {
@@ -73,6 +77,8 @@ struct DGeo {
   // V chunk swizzle: the 16 rows x 32 bytes of one transposing read hit every bank group
   // exactly twice.
   __device__ static int swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
+  // K chunk swizzle: 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
+  __device__ static int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 };
 
 // Scalar state of one block: its buffer resources for K and V.
@@ -93,24 +99,22 @@ __device__ __forceinline__ BlockRes block_res(const DecodeParams& p, int bid, in
   return r;
 }
 
+// Issue one block's loads: K into LDS stage `ks`, V into LDS stage `vs`, full rows per load.
 template <int D>
-struct KFrag {
-  bf16x8 c[DGeo<D>::KC];
-};
-
-// Issue one block's loads: K fragments into registers, V into LDS stage `vs`.
-template <int D>
-__device__ __forceinline__ void issue_block(KFrag<D>& kf, lds_t* vs, const BlockRes& r,
-                                            int koff, const int (&voff)[DGeo<D>::NDMA]) {
+__device__ __forceinline__ void issue_block(lds_t* ks, lds_t* vs, const BlockRes& r,
+                                            const int (&koff)[DGeo<D>::NDMA],
+                                            const int (&voff)[DGeo<D>::NDMA]) {
   using G = DGeo<D>;
 #pragma unroll
-  for (int c = 0; c < G::KC; ++c)
-    kf.c[c] = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k, koff + 64 * c, 0, 0));
+  for (int t = 0; t < G::NDMA; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, ks + t * 1024, 16, koff[t], 0, 0, kStreamOnce);
 #pragma unroll
   for (int t = 0; t < G::NDMA; ++t)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, vs + t * 1024, 16, voff[t], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, vs + t * 1024, 16, voff[t], 0, 0, kStreamOnce);
 }
+
+// lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // vmcnt(n): wait until at most n vector-memory operations of this wave are outstanding.
 template <int N>
@@ -127,8 +131,13 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char vs1[G::VTILE];
   __shared__ __attribute__((aligned(1024))) char vs2[G::VTILE];
   __shared__ __attribute__((aligned(1024))) char vs3[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char ks0[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char ks2[G::VTILE];
+  __shared__ __attribute__((aligned(1024))) char ks3[G::VTILE];
   lds_t* const VS[kStages] = {(lds_t*)vs0, (lds_t*)vs1, (lds_t*)vs2, (lds_t*)vs3};
-  constexpr int kLoadsPerBlock = G::KC + G::NDMA;
+  lds_t* const KS[kStages] = {(lds_t*)ks0, (lds_t*)ks1, (lds_t*)ks2, (lds_t*)ks3};
+  constexpr int kLoadsPerBlock = 2 * G::NDMA;
 
   const int lane = threadIdx.x;
   // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Work unit u = one key range
@@ -152,17 +161,19 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
 
   const int row_bytes = p.Hkv * G::RB;
   const int col = lane & 15, grp = lane >> 4;
-  // K: for MFMA step c, lane holds token `col`, head dims 32c + 8*grp .. +7; one load
-  // instruction covers 16 token rows x 64 contiguous bytes.
-  const int koff = col * row_bytes + (g * D + 8 * grp) * 2;
-  // V: direct load t writes LDS rows RPI*t .. +RPI-1; lane -> (row, swizzled chunk).
-  int voff[G::NDMA];
+  // K and V: direct load t writes LDS rows RPI*t .. +RPI-1 (whole rows, so every load
+  // instruction reads whole cache lines); lane -> (row, swizzled chunk).
+  int koff[G::NDMA], voff[G::NDMA];
 #pragma unroll
   for (int t = 0; t < G::NDMA; ++t) {
     const int row = t * G::RPI + lane / G::CPR;
-    const int chunk = (lane % G::CPR) ^ G::swz(row);
-    voff[t] = row * row_bytes + g * G::RB + chunk * 16;
+    koff[t] = row * row_bytes + g * G::RB + (((lane % G::CPR) ^ G::swz_k(row)) * 16);
+    voff[t] = row * row_bytes + g * G::RB + (((lane % G::CPR) ^ G::swz(row)) * 16);
   }
+  // K fragment reads: for MFMA step c, lane holds token `col`, head dims 32c + 8*grp .. +7.
+  int krd[G::KC];
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c) krd[c] = col * G::RB + (((4 * c + grp) ^ G::swz_k(col)) << 4);
   // V^T fragment reads: group grp reads tokens 4*grp .. +3, dims 16n + 4*(s & 3) per source
   // lane s; the 16 lanes then hold 4 tokens of dims 16n .. 16n+15.
   int vrd[G::NB];
@@ -199,9 +210,8 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
   float m_run = kNegInf, l_run = 0.f;
   const float sl2 = p.sl2;
 
-  KFrag<D> kf[kStages];
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i) issue_block<D>(kf[i], VS[i], res_of(i), koff, voff);
+  for (int i = 0; i < kStages - 1; ++i) issue_block<D>(KS[i], VS[i], res_of(i), koff, voff);
 
   // Block i lives in stage i % kStages; issuing block i + kStages - 1 before computing block i
   // keeps kStages - 1 blocks of loads in flight.  Past the end the loads are empty (size 0) but
@@ -209,12 +219,19 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
   auto step = [&](int i, auto stage) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
     constexpr int NX = (ST + kStages - 1) % kStages;
-    issue_block<D>(kf[NX], VS[NX], res_of(i + kStages - 1), koff, voff);
+    // Stage NX was read by the previous step.  The compiler does not see that the direct loads
+    // write LDS, so it could move them above those reads: wait for every LDS read of this wave
+    // and let nothing be scheduled across this point.
+    wait_lds();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_block<D>(KS[NX], VS[NX], res_of(i + kStages - 1), koff, voff);
     wait_vmem<(kStages - 1) * kLoadsPerBlock>();
     if (i >= n_blk) return;
     f32x4 s = f32x4{};
 #pragma unroll
-    for (int c = 0; c < G::KC; ++c) s = mfma16k32(kf[ST].c[c], qf[c], s);
+    for (int c = 0; c < G::KC; ++c)
+      s = mfma16k32(*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(KS[ST] + krd[c]),
+                    qf[c], s);
     const int tok0 = tok_begin + i * kBS;
     if (tok0 + kBS > L) {
 #pragma unroll
