@@ -12,12 +12,16 @@ fusion, no online softmax):
 * ``attention_ref``     -- materialised three-pass softmax attention (prefill).
 * ``paged_decode_ref``  -- one query row per sequence against a KV cache stored in
                            fixed-size physical blocks addressed through a block table.
+* ``attention_bwd_ref`` -- gradients of the prefill definition with respect to Q, K and V
+                           (chain rule through the row softmax, full P materialised).
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against closed forms,
+Every function is pinned by ``tests/test_oracle_pins.py`` (backward: ``tests/test_oracle_bwd_pins.py``) against closed forms,
 invariances, a pure-Python brute force and a library routine.
 """
 
 from .attention import attention_ref, attention_probs_ref
+from .backward import attention_bwd_ref
 from .paged import paged_decode_ref, gather_paged_kv
 
-__all__ = ["attention_ref", "attention_probs_ref", "paged_decode_ref", "gather_paged_kv"]
+__all__ = ["attention_ref", "attention_probs_ref", "attention_bwd_ref", "paged_decode_ref",
+           "gather_paged_kv"]

@@ -1,0 +1,66 @@
+"""Attention backward in float64, materialised (oracle; test infrastructure).
+
+What it computes: the gradients of the forward definition in ``oracle/attention.py`` --
+O = P V with P the row softmax of S = scale * Q K^T (the "GPU优化" tag page, excerpt "Flash
+Attention解决了什么问题？", 标准注意力计算) -- with respect to Q, K and V, for a given output
+gradient dO.  They are the chain rule written out, with the full probability matrix in memory:
+
+    dV = P^T dO                       (O is linear in V)
+    dP = dO V^T                       (O is linear in P)
+    dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+                                      (the derivative of a row softmax: for p = softmax(s),
+                                       dL/ds = p o (dL/dp - <p, dL/dp>))
+    dQ = scale * dS K,   dK = scale * dS^T Q
+                                      (S = scale * Q K^T is bilinear in Q and K)
+
+The fused kernel never stores P: it rebuilds it from the per-row log-sum-exp the forward
+wrote ("Gemini 3 Flash的注意力内核重写" §4 on recomputation).  This oracle materialises P with
+the forward oracle's three passes instead, so it shares nothing with that recomputation.
+
+Grouped-query heads: kv head g receives the sum of the gradients of the query heads that read
+it.  Padding (per-sequence length L_b): query rows i >= L_b get dQ = 0, keys j >= L_b get
+dK = dV = 0 (they take no part in any visible score).
+"""
+
+import numpy as np
+
+from .attention import _check_shapes, _lengths, _three_pass, _visible_keys
+
+__all__ = ["attention_bwd_ref"]
+
+
+def attention_bwd_ref(q, k, v, dout, scale, causal=False, seq_lens=None):
+    """Gradients (dQ [B,H,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d]) in float64.
+
+    q, dout [B, H, N, d]; k, v [B, Hkv, N, d] (any real dtype; upcast exactly to float64).
+    scale, causal and seq_lens as for ``attention_ref``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    B, H, Hkv, N, d = _check_shapes(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("dout must have the shape of q")
+    group = H // Hkv
+    lens = _lengths(seq_lens, B, N)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    scale = float(scale)
+    for b in range(B):
+        L = lens[b]
+        if L == 0:
+            continue
+        rows = np.arange(L)
+        counts = _visible_keys(rows, L, causal)
+        for h in range(H):
+            g = h // group
+            qb, kb, vb, dob = q[b, h, :L], k[b, g, :L], v[b, g, :L], do[b, h, :L]
+            _, _, p = _three_pass(qb, kb, vb, scale, counts)    # P [L, L], 0 where invisible
+            dv[b, g, :L] += p.T @ dob
+            dp = dob @ vb.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, h, :L] = scale * (ds @ kb)
+            dk[b, g, :L] += scale * (ds.T @ qb)
+    return dq, dk, dv
