@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,decode,copy} [--steps K]   (one kernel, for profilers)
+    python bench.py --only {fwd,fwd_causal,bwd,decode,copy} [--steps K]   (one op, for profilers)
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -113,6 +113,17 @@ def only(args, torch, dev, wf, wd):
         causal = args.only == "fwd_causal"
         fn = lambda: fa_fwd(q, k, v, o, lse, causal=causal)  # noqa: E731
         what = f"fa_fwd B=1 H=8 N=16384 d=128 bf16 causal={causal}"
+    elif args.only == "bwd":
+        from io_aware_attention_02_amd import fa_bwd
+        from io_aware_attention_02_amd.inputs import output_gradient
+        q, k, v, _ = prefill_inputs(wf["B"], wf["H"], wf["Hkv"], wf["N"], wf["d"], "bf16",
+                                    seed=wf["seed"])
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        dout = output_gradient(wf["B"], wf["H"], wf["N"], wf["d"], seed=wf["seed"]).to(dev)
+        o, lse = fa_fwd(q, k, v)
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fn = lambda: fa_bwd(q, k, v, o, lse, dout, gq, gk, gv)  # noqa: E731
+        what = "fa_bwd B=1 H=8 N=16384 d=128 bf16 non-causal"
     elif args.only == "decode":
         dq, kc, vc, table, lens = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
                                                       wd["block_size"], wd["len_lo"], wd["len_hi"],
@@ -142,7 +153,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_causal", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fwd_causal", "bwd", "decode", "copy"], default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -285,6 +296,19 @@ def main():
         f = acc.attention_flops(w4["B"], w4["H"], w4["N"], w4["d"], causal=True, seq_lens=lh)
         extras["gqa_varlen_8k_causal"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
                                           "seq_lens": lh}
+        # Backward (recompute from the forward's LSE) on the headline inputs, both masks.
+        from io_aware_attention_02_amd import fa_bwd, fa_bwd_workspace_bytes
+        from io_aware_attention_02_amd.inputs import output_gradient
+        dout = output_gradient(wf["B"], wf["H"], wf["N"], wf["d"], seed=wf["seed"]).to(dev)
+        wsb = torch.empty(fa_bwd_workspace_bytes(wf["B"], wf["H"], wf["N"]), dtype=torch.uint8,
+                          device=dev)
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        for causal, name in ((False, "backward_16k"), (True, "backward_16k_causal")):
+            ob, lb = fa_fwd(q, k, v, causal=causal)
+            t = _time_calls(torch, lambda: fa_bwd(q, k, v, ob, lb, dout, gq, gk, gv, causal=causal,
+                                                  workspace=wsb), 10)
+            f = acc.attention_bwd_flops(wf["B"], wf["H"], wf["N"], wf["d"], causal=causal)
+            extras[name] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2)}
         out["extras"] = extras
 
     if not args.no_cpu_baseline:

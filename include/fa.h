@@ -1,11 +1,13 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) fused attention library (libfa.so).
  *
- * Two operations, both asynchronous on the caller's HIP stream:
+ * Three operations, all asynchronous on the caller's HIP stream:
  *
  *   fa_fwd           fused, tiled attention forward O = softmax(scale * Q K^T) V with an
  *                    online softmax; the N x N score and probability matrices never reach
  *                    device memory.  Also writes the per-row log-sum-exp.
+ *   fa_bwd           the matching backward (dQ, dK, dV), recomputing the probabilities from
+ *                    the stored log-sum-exp.
  *   fa_paged_decode  one query token per sequence against a KV cache stored in fixed-size
  *                    physical blocks that a block table addresses (non-contiguous gather).
  *
@@ -80,6 +82,41 @@ enum { FA_BF16 = 0, /* bf16 storage, fp32 arithmetic and accumulation on the mat
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int Hkv, int N, int d, float scale, int causal, const int32_t* seq_lens,
                  int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- size in bytes of the device workspace fa_bwd needs (one fp32
+ * per query row: D = rowsum(dO * O)).  Returns 0 for non-positive sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_bwd -- attention backward by recomputation.
+ *
+ * Gradients of O = softmax(scale * Q K^T) V (as defined for fa_fwd) with respect to Q, K and
+ * V, given the output gradient dO.  The probabilities are not stored by the forward: they are
+ * recomputed from q, k and the forward's per-row lse, P = exp(scale * Q K^T - lse) (page
+ * "Gemini 3 Flash的注意力内核重写", §4 on recomputation: the forward keeps each row's maximum
+ * and normaliser so that the backward can rebuild the scores).  With D_i = sum_d dO_id O_id,
+ *   dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale * dS K,   dK = scale * dS^T Q,
+ * summed over the query heads of each kv head for dK and dV.
+ *
+ *   q, o, dout   [B, H, N, d] bf16: the forward's inputs, its output and the output gradient
+ *   k, v         [B, Hkv, N, d] bf16
+ *   lse          [B, H, N] fp32: the lse fa_fwd wrote for these q, k, v (natural log)
+ *   dq           [B, H, N, d] bf16, written (0 for padding rows)
+ *   dk, dv       [B, Hkv, N, d] bf16, written (0 for keys at or past the valid length)
+ *   B, H, Hkv, N, d, scale, causal, seq_lens: as for fa_fwd (d: 64 or 128).
+ *   dtype        FA_BF16 (FA_F32 is not supported by the backward).
+ *   workspace    device buffer of at least fa_bwd_workspace_bytes(B, H, N) bytes, 16-byte
+ *                aligned, owned by the caller; its contents on entry do not matter.  Calls
+ *                that share a workspace must be ordered.
+ *   stream       hipStream_t or NULL.
+ * The result is deterministic: no atomics, a fixed summation order.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                 int d, float scale, int causal, const int32_t* seq_lens, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fa_paged_decode_workspace_bytes -- size in bytes of the device workspace fa_paged_decode

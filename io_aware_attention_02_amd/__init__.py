@@ -1,4 +1,5 @@
-"""Fused attention forward and paged decode for AMD Instinct MI355X (gfx950).
+"""Fused attention forward, its recompute backward and paged decode for AMD Instinct MI355X
+(gfx950).
 
 The compute runs in hand-written HIP kernels behind a small C ABI (``include/fa.h``,
 built as ``libfa.so`` next to this file).  This package is the thin Python binding over it:
@@ -11,6 +12,8 @@ from ._binding import (  # noqa: F401
     FA_BF16,
     FA_F32,
     FaError,
+    fa_bwd,
+    fa_bwd_workspace_bytes,
     fa_fwd,
     fa_paged_decode,
     fa_paged_decode_workspace_bytes,

@@ -16,6 +16,8 @@ __all__ = [
     "FA_BF16",
     "FA_F32",
     "FaError",
+    "fa_bwd",
+    "fa_bwd_workspace_bytes",
     "fa_fwd",
     "fa_paged_decode",
     "fa_paged_decode_workspace_bytes",
@@ -55,6 +57,11 @@ def load_library():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.restype = i32
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp,
+                           i32, vp, sz, vp]
     lib.fa_paged_decode_workspace_bytes.restype = sz
     lib.fa_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_paged_decode.restype = i32
@@ -123,6 +130,51 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, seq_lens=None, s
     if st != 0:
         raise FaError(st, "fa_fwd")
     return o, lse
+
+
+def fa_bwd_workspace_bytes(B, H, N):
+    return int(load_library().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale=None, causal=False,
+           seq_lens=None, workspace=None, stream=None):
+    """Attention backward.  q, o, dout [B,H,N,d] bf16; k, v [B,Hkv,N,d] bf16; lse [B,H,N] fp32
+    as written by fa_fwd for the same inputs.  Returns (dq, dk, dv) shaped like q, k, v.
+
+    ``workspace`` is an optional preallocated uint8 device tensor; if None one is allocated
+    with torch (the library itself never allocates).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_device_tensor(name, t, torch.bfloat16)
+    _check_device_tensor("lse", lse, torch.float32)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or o.shape != q.shape or \
+            dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B,H,N,d] and k, v [B,Hkv,N,d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_device_tensor(name, t, torch.bfloat16)
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must have shape {tuple(like.shape)}")
+    if seq_lens is not None:
+        _check_device_tensor("seq_lens", seq_lens, torch.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_device_tensor("workspace", workspace)
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                    _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)), _ptr(seq_lens),
+                    FA_BF16, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                    _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fa_paged_decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size=16):

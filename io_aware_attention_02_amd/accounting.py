@@ -4,6 +4,8 @@ The counts are the algorithmic ones the throughput figures are quoted in:
 * forward flops: two contractions of 2*N*N*d each per (batch, head), i.e. 4*B*H*N^2*d,
   halved under causal masking; with per-sequence lengths the sum over sequences of
   4*H*L_b^2*d (halved under causal).
+* backward flops: five contractions of the same size (S = Q K^T recomputed, dV = P^T dO,
+  dP = dO V^T, dQ = dS K, dK = dS^T Q), i.e. 2.5 times the forward's.
 * decode bytes: every cached K and V element a step must read (sum of L_b*Hkv*d*2 bytes for
   each of K and V), plus q, o, lse, the block ids in use and the lengths.
 
@@ -17,6 +19,7 @@ import math
 
 __all__ = [
     "attention_flops",
+    "attention_bwd_flops",
     "forward_min_bytes",
     "decode_bytes",
     "decode_flops",
@@ -38,6 +41,11 @@ def attention_flops(B, H, N, d, causal=False, seq_lens=None):
     else:
         f = sum(4 * H * int(L) * int(L) * d for L in seq_lens)
     return f / 2 if causal else f
+
+
+def attention_bwd_flops(B, H, N, d, causal=False, seq_lens=None):
+    """Algorithmic flops of one backward pass: five contractions, 2.5x the forward's."""
+    return 2.5 * attention_flops(B, H, N, d, causal=causal, seq_lens=seq_lens)
 
 
 def forward_min_bytes(B, H, Hkv, N, d, elem_bytes=2):

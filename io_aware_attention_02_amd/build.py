@@ -25,6 +25,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
+# Per-source extras.  The backward kernels run one wave per SIMD with more than 256 live
+# registers; keeping every MFMA accumulator in architectural VGPRs (the extra registers then
+# serve as cheap spill space) avoids copying score tiles out of accumulation registers.
+PER_FILE = {"fa_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc():
@@ -41,7 +45,8 @@ def sources():
 def _compile(src, hipcc, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc, *COMMON, *DEVICE_FLAGS, *lang, "-c", src, "-o", obj]
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [hipcc, *COMMON, *DEVICE_FLAGS, *extra, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
             if "not a recognized feature for this target" not in ln]

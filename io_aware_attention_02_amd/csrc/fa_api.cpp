@@ -72,6 +72,52 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N) { return fa::bwd_workspace_bytes(B, H, N); }
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                 int d, float scale, int causal, const int32_t* seq_lens, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;  // unknown, or fp32 (forward only)
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // Grids: one workgroup per (batch, head, 128 rows), and one per 16 rows of the row pass.
+  const long long tiles = (long long)B * H * ((N + 127) / 128);
+  const long long rows = (long long)B * H * N;
+  if (tiles > INT_MAX || rows / 16 + 1 > INT_MAX) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::bwd_workspace_bytes(B, H, N)) return FA_ERR_INVALID_ARG;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.seq_lens = seq_lens;
+  a.workspace = workspace;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  const hipError_t e = fa::launch_bwd_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_paged_decode_workspace_bytes(int num_seqs, int Hq, int d, int max_blocks_per_seq,
                                        int block_size) {
   return fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);

@@ -36,6 +36,26 @@ struct DecodeArgs {
   void* workspace;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* seq_lens;  // nullptr: every sequence has N valid rows
+  void* workspace;          // D = rowsum(dO * O) [B, H, N] fp32
+  int B, H, Hkv, N, d;
+  float scale;
+  bool causal;
+};
+
+size_t bwd_workspace_bytes(int B, int H, int N);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
 // Tokens per key-range split of the decode kernel and the resulting workspace size.
 constexpr int kDecodeSplitTokens = 512;
 size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size);

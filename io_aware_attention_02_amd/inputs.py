@@ -9,6 +9,8 @@ Recipe (the workload list that the measurements quote):
 * prefill: q, k, v drawn in that order as float32 N(0, 1), then rounded to the storage dtype
   (bf16 round-to-nearest-even, or kept float32); layout [B, H, N, d] / [B, Hkv, N, d].
   With per-sequence lengths, ``seq_lens`` is drawn after v, uniform in [lo, hi].
+* backward: the output gradient dO [B, H, N, d] is drawn from its own generator (seed + 1000)
+  as float32 N(0, 1) rounded to the storage dtype.
 * paged decode: ``seq_lens`` uniform in [lo, hi] first, then a random permutation that places
   each sequence's logical blocks in the pool, then q [S, Hq, d], then the K pool and the V pool
   [num_blocks, block_size, Hkv, d], all N(0, 1) rounded to bf16.  Unused block-table entries
@@ -22,6 +24,7 @@ import torch
 
 __all__ = [
     "prefill_inputs",
+    "output_gradient",
     "varlen_lengths",
     "paged_decode_inputs",
     "WORKLOADS",
@@ -70,6 +73,11 @@ def prefill_inputs(B, H, Hkv, N, d, dtype="bf16", seed=0, len_lo=None, len_hi=No
     if len_lo is not None:
         seq_lens = varlen_lengths(B, len_lo, len_hi, g)
     return q, k, v, seq_lens
+
+
+def output_gradient(B, H, N, d, dtype="bf16", seed=0):
+    """dO [B, H, N, d] on the CPU, from its own generator (seed + 1000)."""
+    return _randn((B, H, N, d), _gen(int(seed) + 1000), _DTYPES[dtype])
 
 
 def varlen_lengths(B, lo, hi, gen):

@@ -32,8 +32,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_bytes",
-                                     "fa_status_str"]
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_paged_decode",
+                                     "fa_paged_decode_workspace_bytes", "fa_status_str"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -80,6 +80,38 @@ def test_fwd_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
 
 
+def test_bwd_workspace_bytes(lib):
+    # one fp32 per query row, rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_bytes(1, 8, 16384) == 8 * 16384 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3) == 256
+    assert lib.fa_bwd_workspace_bytes(0, 8, 16) == 0
+    assert lib.fa_bwd_workspace_bytes(2, 8, -1) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=8, Hkv=2, N=128, d=128,
+             scale=0.1, causal=0, seq_lens=None, dtype=0, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                      a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"],
+                      a["seq_lens"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
+    (dict(dv=None), INVALID), (dict(ws=None), INVALID),
+    (dict(B=0), INVALID), (dict(N=-3), INVALID), (dict(H=8, Hkv=3), INVALID),
+    (dict(dq=P + 8), INVALID), (dict(do=P + 4), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(ws=P + 8), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(wsb=100), INVALID),
+    (dict(dtype=1), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 20, wsb=1 << 62), UNSUPPORTED),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
 def _dec(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, S=4, Hq=32, Hkv=8, d=128, bs=16, M=64,
              nb=256, scale=0.1, ws=P, wsb=1 << 30, stream=None)
@@ -108,6 +140,7 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     # Arguments pass validation, so the call reaches the runtime, which has no device.
     assert _fwd(lib) == HIPERR
     assert _dec(lib) == HIPERR
+    assert _bwd(lib) == HIPERR
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
