@@ -118,6 +118,29 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_t* tile, const TrAddr<D>& ta
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// One 32-row block of a score product: s = rows[0..31] . bf over the head dimension (rows of a
+// K-swizzled tile, B operand in registers), reads kAheadK fragments ahead of their MFMAs.
+template <int D>
+__device__ __forceinline__ void scores_block(f32x16& s, const lds_t* rows, const FragAddr<D>& fa,
+                                             const bf16x8 (&bf)[D / 16]) {
+  using G = Geo<D>;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  s = f32x16{};
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c)
+    s = mfma32(*reinterpret_cast<const lds_bf16x8*>(rows + fa.k[c]), bf[c], s);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAheadK, 0);
+#pragma unroll
+  for (int i = 0; i < G::KC - kAheadK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadK, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
 // Work unit = (batch, kv head): every workgroup of a unit reads the same K/V (dQ) or the same
 // Q/dO of the group (dK/dV), so a unit's workgroups run on one XCD (shared L2); units are
 // spread x, x+8, ... when they divide evenly so every XCD holds the same mix of lengths.
@@ -358,39 +381,46 @@ bwd_dkdv_kernel(BwdParams p) {
   f32x16 dk[G::NB], dv[G::NB];
 #pragma unroll
   for (int n = 0; n < G::NB; ++n) dk[n] = dv[n] = f32x16{};
-  f32x16 sS[2], sP[2];
 
+  // One LDS tile of 64 query rows, in two halves of 32: S = Q K^T and dP = dO V^T for the
+  // half (rows = queries, lane column = key), then per 16-row chunk P and dS and the dV^T, dK^T
+  // updates.  Working in halves keeps only one score block of each product live.
   auto tile = [&](const lds_t* Qc, const lds_t* Oc, int buf, int q0t, auto masked) __attribute__((always_inline)) {
     constexpr bool M = decltype(masked)::value;
-    scores<D>(sS, Qc, fa, kf);  // S[q][key]: rows = queries of the tile, lane column = key
-    scores<D>(sP, Oc, fa, vf);  // dP[q][key]
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      // Rows of chunk jj held by this lane: 16 jj + 4 hh + {0..3} and 16 jj + 8 + 4 hh + {0..3}.
-      const f32x4 la = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 4 * hh]);
-      const f32x4 lb = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 8 + 4 * hh]);
-      const f32x4 da = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 4 * hh]);
-      const f32x4 db = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 8 + 4 * hh]);
-      float pe[8], de[8];
+    for (int hq = 0; hq < 2; ++hq) {
+      f32x16 sS, sP;
+      scores_block<D>(sS, Qc + hq * 32 * G::RB, fa, kf);
+      scores_block<D>(sP, Oc + hq * 32 * G::RB, fa, vf);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float x = sS[jj >> 1][8 * (jj & 1) + t];
-        const float l2 = t < 4 ? la[t & 3] : lb[t & 3];
-        const float dd = t < 4 ? da[t & 3] : db[t & 3];
-        float arg = fmaf(x, sl2, -l2);
-        if constexpr (M) {
-          const int qr = q0t + 16 * jj + 8 * (t >> 2) + 4 * hh + (t & 3);
-          if (key >= L || (CAUSAL && key > qr)) arg = kNegInf;
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int jj = 2 * hq + j2;
+        // Rows of chunk jj held by this lane: 16 jj + 4 hh + {0..3} and 16 jj + 8 + 4 hh + {0..3}.
+        const f32x4 la = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 4 * hh]);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 8 + 4 * hh]);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 4 * hh]);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 8 + 4 * hh]);
+        float pe[8], de[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = sS[8 * j2 + t];
+          const float l2 = t < 4 ? la[t & 3] : lb[t & 3];
+          const float dd = t < 4 ? da[t & 3] : db[t & 3];
+          float arg = fmaf(x, sl2, -l2);
+          if constexpr (M) {
+            const int qr = q0t + 16 * jj + 8 * (t >> 2) + 4 * hh + (t & 3);
+            if (key >= L || (CAUSAL && key > qr)) arg = kNegInf;
+          }
+          pe[t] = fast_exp2(arg);
+          de[t] = pe[t] * (sP[8 * j2 + t] - dd);
         }
-        pe[t] = fast_exp2(arg);
-        de[t] = pe[t] * (sP[jj >> 1][8 * (jj & 1) + t] - dd);
-      }
-      const bf16x8 pf = pack_bf16x8(pe);
-      const bf16x8 dsf = pack_bf16x8(de);
+        const bf16x8 pf = pack_bf16x8(pe);
+        const bf16x8 dsf = pack_bf16x8(de);
 #pragma unroll
-      for (int n = 0; n < G::NB; ++n) {
-        dv[n] = mfma32(tr_frag<D>(Oc, ta, n, jj), pf, dv[n]);
-        dk[n] = mfma32(tr_frag<D>(Qc, ta, n, jj), dsf, dk[n]);
+        for (int n = 0; n < G::NB; ++n) {
+          dv[n] = mfma32(tr_frag<D>(Oc, ta, n, jj), pf, dv[n]);
+          dk[n] = mfma32(tr_frag<D>(Qc, ta, n, jj), dsf, dk[n]);
+        }
       }
     }
   };
