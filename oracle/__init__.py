@@ -12,6 +12,8 @@ fusion, no online softmax):
 * ``attention_ref``     -- materialised three-pass softmax attention (prefill).
 * ``paged_decode_ref``  -- one query row per sequence against a KV cache stored in
                            fixed-size physical blocks addressed through a block table.
+* ``paged_prefill_ref`` -- the newest Q_b tokens of each sequence (chunked prefill) against the
+                           same paged cache, causal with the offset L_b - Q_b.
 * ``attention_bwd_ref`` -- gradients of the prefill definition with respect to Q, K and V
                            (chain rule through the row softmax, full P materialised).
 
@@ -21,7 +23,7 @@ invariances, a pure-Python brute force and a library routine.
 
 from .attention import attention_ref, attention_probs_ref
 from .backward import attention_bwd_ref
-from .paged import paged_decode_ref, gather_paged_kv
+from .paged import paged_decode_ref, paged_prefill_ref, gather_paged_kv
 
 __all__ = ["attention_ref", "attention_probs_ref", "attention_bwd_ref", "paged_decode_ref",
-           "gather_paged_kv"]
+           "paged_prefill_ref", "gather_paged_kv"]

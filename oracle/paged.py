@@ -14,11 +14,20 @@ Layouts (readings listed in the design doc):
 * block_table [S, max_blocks] integer physical block ids; entry t // block_size holds token t
 * seq_lens [S]; a sequence of length 0 yields O = 0, LSE = -inf.
 Query head h reads kv head h // (Hq // Hkv).
+
+Chunked prefill against the cache (``paged_prefill_ref``): the query chunk of sequence b is its
+newest Q_b tokens, positions L_b - Q_b .. L_b - 1, whose keys and values are already in the
+cache; query i sees the cached tokens 0 .. L_b - Q_b + i (causal with that offset).  This is
+the chunked prefill of "LLM inference optimisation" §3.2 (a long prompt processed in pieces
+against the cache built so far); with Q_b = 1 it is one decode step.  Layout (head-major, as
+the prefill forward): q [S, Hq, Qmax, d]; rows i >= Q_b are padding and get O = 0, LSE = -inf.
 """
 
 import numpy as np
 
-__all__ = ["gather_paged_kv", "paged_decode_ref"]
+from .attention import _three_pass
+
+__all__ = ["gather_paged_kv", "paged_decode_ref", "paged_prefill_ref"]
 
 
 def gather_paged_kv(cache, block_table_row, length):
@@ -63,4 +72,33 @@ def paged_decode_ref(q, k_cache, v_cache, block_table, seq_lens, scale):
             # pass 3: normalise and weight the values
             o[b, h] = (e / l) @ vb[:, g, :]
             lse[b, h] = m + np.log(l)
+    return o, lse
+
+
+def paged_prefill_ref(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale):
+    """Chunked prefill: O [S, Hq, Qmax, d] and LSE [S, Hq, Qmax] in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    S, Hq, Qmax, d = q.shape
+    Hkv = k_cache.shape[2]
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d or Hq % Hkv != 0:
+        raise ValueError("inconsistent shapes")
+    group = Hq // Hkv
+    lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
+    qls = [int(x) for x in np.asarray(q_lens).reshape(-1)]
+    o = np.zeros((S, Hq, Qmax, d))
+    lse = np.full((S, Hq, Qmax), -np.inf)
+    for b in range(S):
+        L, Q = lens[b], qls[b]
+        if Q > L or Q > Qmax:
+            raise ValueError("q_lens must not exceed seq_lens or the query rows")
+        if Q == 0:
+            continue
+        kb = gather_paged_kv(k_cache, block_table[b], L)    # [L, Hkv, d]
+        vb = gather_paged_kv(v_cache, block_table[b], L)
+        counts = (L - Q) + np.arange(Q) + 1                  # keys visible to each query row
+        for h in range(Hq):
+            g = h // group
+            ob, lb, _ = _three_pass(q[b, h, :Q], kb[:, g, :], vb[:, g, :], float(scale), counts)
+            o[b, h, :Q] = ob
+            lse[b, h, :Q] = lb
     return o, lse

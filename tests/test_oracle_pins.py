@@ -341,3 +341,39 @@ def test_paged_decode_brute_force_and_empty_sequence():
             for t in range(d):
                 assert abs(o[b, h, t] - math.fsum(wj * float(r[t]) for wj, r in zip(w, rowsv))) < 1e-12
             assert abs(l[b, h] - lse) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------------
+# chunked prefill against the paged cache
+# ---------------------------------------------------------------------------------------------
+
+def test_paged_prefill_equals_the_last_rows_of_causal_attention():
+    # The chunk's rows are the last Q rows of causal attention over the whole gathered sequence.
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(55)
+    S, Hq, Hkv, d, bs = 3, 4, 2, 8, 4
+    lens, qls, Qmax = [13, 7, 16], [5, 6, 1], 6
+    _, kc, vc, table = _paged_case(rng, S, Hq, Hkv, d, bs, lens)
+    q = _rand(rng, S, Hq, Qmax, d)
+    o, l = paged_prefill_ref(q, kc, vc, table, lens, qls, 0.3)
+    for b, (L, Q) in enumerate(zip(lens, qls)):
+        kb = gather_paged_kv(kc, table[b], L).transpose(1, 0, 2)[None]   # [1, Hkv, L, d]
+        vb = gather_paged_kv(vc, table[b], L).transpose(1, 0, 2)[None]
+        qq = _rand(rng, 1, Hq, L, d)
+        qq[0, :, L - Q:] = q[b, :, :Q]
+        oc, lc = attention_ref(qq, kb, vb, 0.3, causal=True, rows=list(range(L - Q, L)))
+        np.testing.assert_allclose(o[b, :, :Q], oc[0], atol=1e-12)
+        np.testing.assert_allclose(l[b, :, :Q], lc[0], atol=1e-12)
+        assert not o[b, :, Q:].any() and np.isneginf(l[b, :, Q:]).all()
+
+
+def test_paged_prefill_of_one_token_is_a_decode_step():
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(56)
+    S, Hq, Hkv, d, bs = 3, 8, 2, 16, 4
+    lens = [1, 13, 16]
+    q, kc, vc, table = _paged_case(rng, S, Hq, Hkv, d, bs, lens)
+    od, ld = paged_decode_ref(q, kc, vc, table, lens, 0.25)
+    op, lp = paged_prefill_ref(q[:, :, None, :], kc, vc, table, lens, [1, 1, 1], 0.25)
+    np.testing.assert_allclose(op[:, :, 0], od, atol=1e-12)
+    np.testing.assert_allclose(lp[:, :, 0], ld, atol=1e-12)
