@@ -1,7 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) fused attention library (libfa.so).
  *
- * Three operations, all asynchronous on the caller's HIP stream:
+ * Four operations, all asynchronous on the caller's HIP stream:
  *
  *   fa_fwd           fused, tiled attention forward O = softmax(scale * Q K^T) V with an
  *                    online softmax; the N x N score and probability matrices never reach
@@ -10,6 +10,7 @@
  *                    the stored log-sum-exp.
  *   fa_paged_decode  one query token per sequence against a KV cache stored in fixed-size
  *                    physical blocks that a block table addresses (non-contiguous gather).
+ *   fa_paged_prefill a chunk of each sequence's newest tokens against the same paged cache.
  *
  * Conventions for every entry point
  *   - Every data pointer is a caller-owned DEVICE pointer (e.g. from torch).  The library
@@ -160,6 +161,34 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
                           float* lse, int num_seqs, int Hq, int Hkv, int d, int block_size,
                           int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * fa_paged_prefill -- chunked prefill against a paged KV cache.
+ *
+ * For each sequence b the query chunk is its newest Q_b = q_lens[b] tokens, at positions
+ * L_b - Q_b .. L_b - 1 of the sequence (L_b = seq_lens[b]), whose keys and values are already
+ * in the cache.  Query row i attends to the cached tokens 0 .. L_b - Q_b + i (causal with that
+ * offset) -- the chunked prefill of the LLM inference-optimisation article (ijyty.com) §3.2, a
+ * long prompt processed piece by piece against the cache built so far; Q_b = 1 is one decode
+ * step.  The cache and block table are as for fa_paged_decode; the kernel is fa_fwd's, with its
+ * key/value tiles gathered block by block through the table.
+ *
+ *   q            [num_seqs, Hq, max_q, d] bf16 (head-major, as fa_fwd's q); rows i >= Q_b are
+ *                padding
+ *   k_cache, v_cache, block_table: as for fa_paged_decode
+ *   seq_lens     [num_seqs] int32 (device): tokens in the cache, clamped to
+ *                [0, max_blocks_per_seq * block_size]
+ *   q_lens       [num_seqs] int32 (device): chunk lengths, clamped to [0, min(L_b, max_q)]
+ *   o            [num_seqs, Hq, max_q, d] bf16, written (0 in padding rows)
+ *   lse          [num_seqs, Hq, max_q] fp32, written (natural log; -inf in padding rows)
+ *   Hq % Hkv == 0.  d: 64 or 128.  block_size: 16.  scale finite and >= 0.
+ *   stream       hipStream_t or NULL.
+ */
+fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* q_lens, void* o, float* lse, int num_seqs, int max_q,
+                           int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                           int num_blocks, float scale, void* stream);
 
 /* fa_status_str -- static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);

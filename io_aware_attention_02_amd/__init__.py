@@ -1,5 +1,5 @@
-"""Fused attention forward, its recompute backward and paged decode for AMD Instinct MI355X
-(gfx950).
+"""Fused attention forward, its recompute backward, paged decode and chunked prefill against
+the paged cache, for AMD Instinct MI355X (gfx950).
 
 The compute runs in hand-written HIP kernels behind a small C ABI (``include/fa.h``,
 built as ``libfa.so`` next to this file).  This package is the thin Python binding over it:
@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     fa_fwd,
     fa_paged_decode,
     fa_paged_decode_workspace_bytes,
+    fa_paged_prefill,
     fa_status_str,
     library_path,
     load_library,

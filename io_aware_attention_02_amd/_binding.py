@@ -21,6 +21,7 @@ __all__ = [
     "fa_fwd",
     "fa_paged_decode",
     "fa_paged_decode_workspace_bytes",
+    "fa_paged_prefill",
     "fa_status_str",
     "library_path",
     "load_library",
@@ -67,6 +68,9 @@ def load_library():
     lib.fa_paged_decode.restype = i32
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, sz, vp]
+    lib.fa_paged_prefill.restype = i32
+    lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, vp]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [i32]
     _LIB = lib
@@ -219,4 +223,36 @@ def fa_paged_decode(q, k_cache, v_cache, block_table, seq_lens, o=None, lse=None
                              _stream(stream))
     if st != 0:
         raise FaError(st, "fa_paged_decode")
+    return o, lse
+
+
+def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, q_lens, o=None, lse=None,
+                     scale=None, stream=None):
+    """Chunked prefill against a paged cache.  q [S,Hq,Qmax,d] bf16 (each sequence's newest
+    q_lens[b] tokens, head-major); caches [P,bs,Hkv,d] bf16; block_table [S,M], seq_lens [S],
+    q_lens [S] int32.  Returns (o [S,Hq,Qmax,d] bf16, lse [S,Hq,Qmax] fp32)."""
+    lib = load_library()
+    _check_device_tensor("q", q, torch.bfloat16)
+    _check_device_tensor("k_cache", k_cache, torch.bfloat16)
+    _check_device_tensor("v_cache", v_cache, torch.bfloat16)
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens), ("q_lens", q_lens)):
+        _check_device_tensor(name, t, torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape or block_table.dim() != 2:
+        raise ValueError("q [S,Hq,Qmax,d], caches [P,bs,Hkv,d], block_table [S,M]")
+    S, Hq, Qmax, d = q.shape
+    P, bs, Hkv, _ = k_cache.shape
+    M = block_table.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, Hq, Qmax), dtype=torch.float32, device=q.device)
+    _check_device_tensor("o", o, torch.bfloat16)
+    _check_device_tensor("lse", lse, torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.fa_paged_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                              _ptr(seq_lens), _ptr(q_lens), _ptr(o), _ptr(lse), S, Qmax, Hq, Hkv,
+                              d, bs, M, P, float(scale), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_paged_prefill")
     return o, lse

@@ -72,6 +72,51 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* q_lens, void* o, float* lse, int num_seqs, int max_q,
+                           int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                           int num_blocks, float scale, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !q_lens || !o || !lse)
+    return FA_ERR_INVALID_ARG;
+  if (num_seqs <= 0 || max_q <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(q_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (block_size != 16) return FA_ERR_UNSUPPORTED;
+  // One workgroup per (sequence, query head, tile of >= 128 query rows); key positions and
+  // offsets in 32-bit integers.
+  const long long tiles = (long long)num_seqs * Hq * ((max_q + 127) / 128);
+  if (tiles > INT_MAX || (long long)max_blocks_per_seq * block_size > INT_MAX / 2)
+    return FA_ERR_UNSUPPORTED;
+
+  fa::PagedPrefillArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
+  a.o = o;
+  a.lse = lse;
+  a.S = num_seqs;
+  a.max_q = max_q;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale = scale;
+  const hipError_t e = fa::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N) { return fa::bwd_workspace_bytes(B, H, N); }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -54,14 +54,55 @@ constexpr float kMaxProb = 65536.f;    // 2^kTau
 
 struct Params {
   const bf16* q;
-  const bf16* k;
-  const bf16* v;
+  const bf16* k;  // paged: the key cache [num_blocks, 16, Hkv, d]
+  const bf16* v;  // paged: the value cache
   bf16* o;
   float* lse;
-  const int32_t* seq_lens;
-  int H, group, Hkv, N, n_qt, total;
+  const int32_t* seq_lens;  // paged: tokens in the cache per sequence
+  const int32_t* table;     // paged: block table [B, max_blocks]
+  const int32_t* q_lens;    // paged: query rows per sequence (its newest tokens)
+  int H, group, Hkv, N, n_qt, total, max_blocks;
   float sl2;  // scale * log2(e): scores go to the exponent base 2
 };
+
+constexpr int kPageRows = 16;  // tokens per physical block of the paged cache
+
+// Per-lane byte offsets of this wave's direct loads when the tile rows come from a paged cache:
+// tile row r lives at slot r % 16 of its block, rows of one block are Hkv * d elements apart,
+// and the chunk swizzle is the tile's (by tile row).  Each load covers rows of one block.
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void tile_offsets_paged(int* off, int wave, int lane, int row_elems) {
+  using G = Geo<D>;
+  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
+#pragma unroll
+  for (int t = 0; t < NI_W; ++t) {
+    const int row = (wave * NI_W + t) * G::RPI + lane / G::CPR;
+    const int chunk = (lane % G::CPR) ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
+    off[t] = (row % kPageRows) * row_elems * 2 + chunk * 16;
+  }
+}
+
+// Direct global -> LDS copy of this wave's rows of one tile from a paged cache: all of them lie
+// in one physical block (bid), whose buffer resource ends at the sequence's last valid token.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_paged(lds_t* dst, const bf16* cache, int bid, int g,
+                                                int valid_rows, int Hkv, const int* off, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
+  const int bytes = __builtin_amdgcn_readfirstlane(
+      valid_rows > 0 ? ((valid_rows - 1) * Hkv * D + D) * 2 : 0);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(
+      cache + ((size_t)bid * kPageRows * Hkv + g) * D);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
+#pragma unroll
+  for (int t = 0; t < NI_W; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * NI_W + t) * 1024, 16, off[t],
+                                             0, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   float m0 = s[0][0], m1 = s[1][0];
@@ -137,7 +178,7 @@ __device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* 
   return rs;
 }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, bool PAGED>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(Params p) {
   using G = Geo<D>;
@@ -174,8 +215,13 @@ fwd_bf16_kernel(Params p) {
   const int H = p.H, N = p.N;
   const int h = g * p.group + hi;
   const int bh = b * H + h;
+  // L: keys of this sequence.  Lq: its valid query rows, which sit at key positions off ..
+  // off + Lq - 1 (a paged prefill chunk is the sequence's newest Lq tokens; otherwise off = 0).
   int L = N;
-  if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
+  if constexpr (PAGED) L = min(max(p.seq_lens[b], 0), p.max_blocks * kPageRows);
+  else if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
+  const int Lq = PAGED ? min(max(p.q_lens[b], 0), min(L, N)) : L;
+  const int off = PAGED ? L - Lq : 0;
 
   const int q0 = qt * kBM;
   const bf16* Qg = p.q + (size_t)bh * N * D;
@@ -184,7 +230,7 @@ fwd_bf16_kernel(Params p) {
   bf16* Og = p.o + (size_t)bh * N * D;
   float* LSEg = p.lse + (size_t)bh * N;
 
-  if (q0 >= L) {  // every row of this tile is padding: O = 0, LSE = -inf
+  if (q0 >= Lq) {  // every row of this tile is padding: O = 0, LSE = -inf
     const int rows = min(kBM, N - q0);
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int i = tid; i < rows * G::CPR; i += kThreads)
@@ -193,27 +239,56 @@ fwd_bf16_kernel(Params p) {
     return;
   }
 
-  const int kv_end = CAUSAL ? min(L, q0 + kBM) : L;   // keys this workgroup needs
+  const int kv_end = CAUSAL ? min(L, off + q0 + kBM) : L;   // keys this workgroup needs
   const int n_kt = (kv_end + kBN - 1) / kBN;
   const int qw0 = q0 + wave * kWQ;
   const int qrow = qw0 + c32;
   // Tiles this wave needs (fewer than n_kt on the causal diagonal).
-  const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
+  const int n_kw = CAUSAL ? min(n_kt, (min(L, off + qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
   const float sl2 = p.sl2;
   int koff[NI_W], voff[NI_W];
-  tile_offsets<D, NW, false>(koff, wave, lane);
-  tile_offsets<D, NW, true>(voff, wave, lane);
+  if constexpr (PAGED) {
+    tile_offsets_paged<D, NW, false>(koff, wave, lane, p.Hkv * D);
+    tile_offsets_paged<D, NW, true>(voff, wave, lane, p.Hkv * D);
+  } else {
+    tile_offsets<D, NW, false>(koff, wave, lane);
+    tile_offsets<D, NW, true>(voff, wave, lane);
+  }
+  // Paged: this wave's rows of every tile lie in one block, block `wblk` of the tile's
+  // kBN / 16; its id for tile j + 1 is fetched one tile ahead (bid_next).
+  const int wblk = wave * NI_W * G::RPI / kPageRows;
+  const int* trow = PAGED ? p.table + (size_t)b * p.max_blocks : nullptr;
+  auto block_id = [&](int jt) __attribute__((always_inline)) {
+    const int blk = jt * (kBN / kPageRows) + wblk;
+    return blk * kPageRows < L ? __builtin_amdgcn_readfirstlane(trow[blk]) : 0;
+  };
+  int bid_next = 0;
+  auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt, int bid) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      const int valid = min(max(L - (jt * kBN + wblk * kPageRows), 0), kPageRows);
+      load_tile_paged<D, NW>(Kd, p.k, bid, g, valid, p.Hkv, koff, wave);
+      load_tile_paged<D, NW>(Vd, p.v, bid, g, valid, p.Hkv, voff, wave);
+    } else {
+      load_tile<D, NW>(Kd, Kg, jt * kBN, L, koff, wave);
+      load_tile<D, NW>(Vd, Vg, jt * kBN, L, voff, wave);
+    }
+  };
 
   // Issue the first loads before anything else: K_0 and V_0.
-  load_tile<D, NW>(K0, Kg, 0, L, koff, wave);
-  load_tile<D, NW>(V0, Vg, 0, L, voff, wave);
+  if constexpr (PAGED) {
+    load_kv(K0, V0, 0, block_id(0));
+    if (1 < n_kt) bid_next = block_id(1);
+  } else {
+    load_kv(K0, V0, 0, 0);
+  }
 
-  // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel.
+  // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel; zero for padding
+  // rows, so that whatever they hold (NaN included) cannot reach their zero output.
   bf16x8 qf[G::KC];
 #pragma unroll
   for (int c = 0; c < G::KC; ++c) {
-    qf[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
-                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    qf[c] = qrow < Lq ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
+                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
   const FragAddr<D> fa = frag_addr<D>(lane);
 
@@ -241,7 +316,7 @@ fwd_bf16_kernel(Params p) {
     constexpr bool M = decltype(masked)::value;
     constexpr int MODE = decltype(mode)::value;
     scores<D>(sA, Kc, fa, qf);
-    if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
+    if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow + off, hh);
     if constexpr (MODE == FAST) {
       // No tile maximum: every probability is at most the lane's share of the tile's row sum,
       // so that sum exceeding 2^kTau is the test that some score outgrew the reference.
@@ -268,7 +343,7 @@ fwd_bf16_kernel(Params p) {
   // buffer is fixed per instantiation, so every LDS access refers to one known buffer and the
   // compiler never waits for the loads in flight.  Tiles [0, n_main) need no mask for any wave
   // of the workgroup; the remaining ones (the causal diagonal, the ragged end) are masked.
-  const int n_main = CAUSAL ? min(q0, L) / kBN : L / kBN;
+  const int n_main = CAUSAL ? min(off + q0, L) / kBN : L / kBN;
   auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(parity)::value;
     lds_t* const Kc = ODD ? K1 : K0;
@@ -276,8 +351,10 @@ fwd_bf16_kernel(Params p) {
     lds_t* const Kn = ODD ? K0 : K1;
     lds_t* const Vn = ODD ? V0 : V1;
     if (j + 1 < n_kt) {
-      load_tile<D, NW>(Kn, Kg, (j + 1) * kBN, L, koff, wave);
-      load_tile<D, NW>(Vn, Vg, (j + 1) * kBN, L, voff, wave);
+      load_kv(Kn, Vn, j + 1, bid_next);
+      if constexpr (PAGED) {
+        if (j + 2 < n_kt) bid_next = block_id(j + 2);
+      }
     }
     if (j < n_kw) tile(Kc, Vc, j * kBN, masked, mode);
     wait_loads();
@@ -315,15 +392,19 @@ fwd_bf16_kernel(Params p) {
     for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
     m_run = kNegInf;
     l_run = 0.f;
-    load_tile<D, NW>(K0, Kg, 0, L, koff, wave);
-    load_tile<D, NW>(V0, Vg, 0, L, voff, wave);
+    if constexpr (PAGED) {
+      load_kv(K0, V0, 0, block_id(0));
+      if (1 < n_kt) bid_next = block_id(1);
+    } else {
+      load_kv(K0, V0, 0, 0);
+    }
     run(std::integral_constant<int, SAFE>{});
   }
 
   // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
   const float lt = add_xor32(l_run);
   if (qrow < N) {
-    const bool valid = qrow < L;
+    const bool valid = qrow < Lq;
     const float inv = valid ? 1.f / lt : 0.f;
 #pragma unroll
     for (int n = 0; n < G::NB; ++n) {
@@ -348,6 +429,9 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.o = static_cast<bf16*>(a.o);
   p.lse = a.lse;
   p.seq_lens = a.seq_lens;
+  p.table = nullptr;
+  p.q_lens = nullptr;
+  p.max_blocks = 0;
   p.H = a.H;
   p.group = a.H / a.Hkv;
   p.Hkv = a.Hkv;
@@ -359,16 +443,52 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   if (wide >= kCUs) {
     p.n_qt = (a.N + 8 * kWQ - 1) / (8 * kWQ);
     p.total = a.B * a.H * p.n_qt;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8, false>), dim3(p.total), dim3(64 * 8), 0, stream, p);
   } else {
     p.n_qt = (a.N + 4 * kWQ - 1) / (4 * kWQ);
     p.total = a.B * a.H * p.n_qt;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3(p.total), dim3(64 * 4), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, false>), dim3(p.total), dim3(64 * 4), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+// Chunked prefill against the paged cache: the same kernel, K/V tiles gathered through the
+// block table, causal with each sequence's offset L_b - Q_b.
+template <int D>
+hipError_t launch_paged(const PagedPrefillArgs& a, hipStream_t stream) {
+  Params p;
+  p.q = static_cast<const bf16*>(a.q);
+  p.k = static_cast<const bf16*>(a.k_cache);
+  p.v = static_cast<const bf16*>(a.v_cache);
+  p.o = static_cast<bf16*>(a.o);
+  p.lse = a.lse;
+  p.seq_lens = a.seq_lens;
+  p.table = a.block_table;
+  p.q_lens = a.q_lens;
+  p.H = a.Hq;
+  p.group = a.Hq / a.Hkv;
+  p.Hkv = a.Hkv;
+  p.N = a.max_q;
+  p.max_blocks = a.max_blocks;
+  p.sl2 = a.scale * kLog2e;
+  const long long wide = (long long)a.S * a.Hq * ((a.max_q + 8 * kWQ - 1) / (8 * kWQ));
+  if (wide >= kCUs) {
+    p.n_qt = (a.max_q + 8 * kWQ - 1) / (8 * kWQ);
+    p.total = a.S * a.Hq * p.n_qt;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 8, true>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+  } else {
+    p.n_qt = (a.max_q + 4 * kWQ - 1) / (4 * kWQ);
+    p.total = a.S * a.Hq * p.n_qt;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4, true>), dim3(p.total), dim3(64 * 4), 0, stream, p);
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
+  return a.d == 128 ? launch_paged<128>(a, stream) : launch_paged<64>(a, stream);
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);

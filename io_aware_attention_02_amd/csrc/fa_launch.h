@@ -36,6 +36,21 @@ struct DecodeArgs {
   void* workspace;
 };
 
+struct PagedPrefillArgs {
+  const void* q;  // [S, Hq, max_q, d]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* q_lens;
+  void* o;     // [S, Hq, max_q, d]
+  float* lse;  // [S, Hq, max_q]
+  int S, max_q, Hq, Hkv, d, max_blocks;
+  float scale;
+};
+
+hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream);
+
 struct BwdArgs {
   const void* q;
   const void* k;

@@ -9,6 +9,9 @@ Recipe (the workload list that the measurements quote):
 * prefill: q, k, v drawn in that order as float32 N(0, 1), then rounded to the storage dtype
   (bf16 round-to-nearest-even, or kept float32); layout [B, H, N, d] / [B, Hkv, N, d].
   With per-sequence lengths, ``seq_lens`` is drawn after v, uniform in [lo, hi].
+* chunked prefill against the paged cache: the decode recipe for the lengths, the block
+  placement and the pools, except that q is [S, Hq, Qmax, d]; the chunk lengths q_lens are
+  drawn last, uniform in [1, min(Qmax, L_b)] (0 for an empty sequence), unless given.
 * backward: the output gradient dO [B, H, N, d] is drawn from its own generator (seed + 1000)
   as float32 N(0, 1) rounded to the storage dtype.
 * paged decode: ``seq_lens`` uniform in [lo, hi] first, then a random permutation that places
@@ -25,6 +28,7 @@ import torch
 __all__ = [
     "prefill_inputs",
     "output_gradient",
+    "paged_prefill_inputs",
     "varlen_lengths",
     "paged_decode_inputs",
     "WORKLOADS",
@@ -40,6 +44,9 @@ WORKLOADS = {
                           len_lo=2048, len_hi=8192),
     "paged_decode": dict(S=64, Hq=32, Hkv=8, d=128, block_size=16, len_lo=512, len_hi=32768,
                          seed=5),
+    # chunked prefill against the paged cache: chunks of up to 1024 new tokens
+    "paged_prefill": dict(S=16, Hq=32, Hkv=8, d=128, max_q=1024, block_size=16, len_lo=1024,
+                          len_hi=32768, seed=6),
 }
 
 _DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -113,3 +120,31 @@ def paged_decode_inputs(S, Hq, Hkv, d, block_size=16, len_lo=512, len_hi=32768, 
     k_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
     v_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
     return q, k_cache, v_cache, table, lens.to(torch.int32)
+
+
+def paged_prefill_inputs(S, Hq, Hkv, d, max_q, block_size=16, len_lo=512, len_hi=32768, seed=0,
+                         seq_lens=None, q_lens=None, spare_blocks=0):
+    """(q [S,Hq,max_q,d], k_cache, v_cache, block_table, seq_lens, q_lens) on the CPU."""
+    g = _gen(seed)
+    if seq_lens is None:
+        lens = torch.randint(int(len_lo), int(len_hi) + 1, (S,), generator=g, dtype=torch.int64)
+    else:
+        lens = torch.as_tensor(list(seq_lens), dtype=torch.int64)
+    nblk = [int(math.ceil(int(x) / block_size)) for x in lens]
+    max_blocks = max(1, max(nblk))
+    pool = sum(nblk) + int(spare_blocks)
+    perm = torch.randperm(max(pool, 1), generator=g, dtype=torch.int64)[:pool]
+    table = torch.full((S, max_blocks), -1, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+    q = _randn((S, Hq, max_q, d), g, torch.bfloat16)
+    k_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
+    v_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
+    if q_lens is None:
+        ql = [int(torch.randint(1, max(1, min(max_q, int(L))) + 1, (1,), generator=g)) if int(L) > 0
+              else 0 for L in lens]
+    else:
+        ql = list(q_lens)
+    return q, k_cache, v_cache, table, lens.to(torch.int32), torch.as_tensor(ql, dtype=torch.int32)

@@ -33,7 +33,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_paged_decode",
-                                     "fa_paged_decode_workspace_bytes", "fa_status_str"]
+                                     "fa_paged_decode_workspace_bytes", "fa_paged_prefill",
+                                     "fa_status_str"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -112,6 +113,29 @@ def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
+def _pre(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, sl=P, ql=P, o=P, lse=P, S=4, Q=64, Hq=32, Hkv=8, d=128, bs=16,
+             M=64, nb=256, scale=0.1, stream=None)
+    a.update(kw)
+    return lib.fa_paged_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["ql"], a["o"], a["lse"],
+                                a["S"], a["Q"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["M"], a["nb"],
+                                a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(bt=None), INVALID),
+    (dict(sl=None), INVALID), (dict(ql=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(S=0), INVALID), (dict(Q=0), INVALID), (dict(M=-1), INVALID),
+    (dict(Hq=32, Hkv=5), INVALID), (dict(scale=math.inf), INVALID), (dict(q=P + 8), INVALID),
+    (dict(ql=P + 2), INVALID), (dict(lse=P + 1), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(bs=8), UNSUPPORTED),
+    (dict(S=1 << 20, Q=1 << 20, Hq=1 << 8, Hkv=1 << 8), UNSUPPORTED),
+    (dict(M=1 << 28), UNSUPPORTED),
+])
+def test_paged_prefill_rejects(lib, kw, status):
+    assert _pre(lib, **kw) == status
+
+
 def _dec(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, S=4, Hq=32, Hkv=8, d=128, bs=16, M=64,
              nb=256, scale=0.1, ws=P, wsb=1 << 30, stream=None)
@@ -141,6 +165,7 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     assert _fwd(lib) == HIPERR
     assert _dec(lib) == HIPERR
     assert _bwd(lib) == HIPERR
+    assert _pre(lib) == HIPERR
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -114,6 +114,7 @@ def test_nan_poisoned_padding_stays_out():
     q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=8)
     lens = torch.tensor([200, 77], dtype=torch.int32)
     for b, L in enumerate(lens.tolist()):
+        q[b, :, L:] = float("nan")
         k[b, :, L:] = float("nan")
         v[b, :, L:] = float("nan")
     for causal in (False, True):
