@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,bwd,decode,copy} [--steps K]   (one op, for profilers)
+    python bench.py --only {fwd,fwd_causal,bwd,prefill_paged,decode,copy} [--steps K]   (one op)
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -33,16 +33,18 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 def _profiled_traffic(kernel):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json), or None when
-    the kernel's source has changed since the counters were taken."""
+    any source of the kernel has changed since the counters were taken."""
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     with open(PROFILE_TRAFFIC) as f:
         entry = json.load(f).get(kernel)
     if not entry:
         return None
-    with open(os.path.join(ROOT, entry["source"]), "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    return entry["hbm_bytes_per_launch"] if digest == entry["source_sha256_16"] else None
+    h = hashlib.sha256()
+    for src in entry["sources"]:  # the kernel's file and the headers it is built from
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return entry["hbm_bytes_per_launch"] if h.hexdigest()[:16] == entry["sources_sha256_16"] else None
 
 
 def _events(torch):
@@ -124,6 +126,15 @@ def only(args, torch, dev, wf, wd):
         gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         fn = lambda: fa_bwd(q, k, v, o, lse, dout, gq, gk, gv)  # noqa: E731
         what = "fa_bwd B=1 H=8 N=16384 d=128 bf16 non-causal"
+    elif args.only == "prefill_paged":
+        from io_aware_attention_02_amd import fa_paged_prefill
+        from io_aware_attention_02_amd.inputs import WORKLOADS, paged_prefill_inputs
+        w5 = WORKLOADS["paged_prefill"]
+        ts = paged_prefill_inputs(w5["S"], w5["Hq"], w5["Hkv"], w5["d"], w5["max_q"],
+                                  w5["block_size"], w5["len_lo"], w5["len_hi"], seed=w5["seed"])
+        pq, pkc, pvc, ptb, psl, pql = (t.to(dev) for t in ts)
+        fn = lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql)  # noqa: E731
+        what = "fa_paged_prefill 16 seqs, chunks <= 1024 of contexts U[1024,32768], Hq=32 Hkv=8"
     elif args.only == "decode":
         dq, kc, vc, table, lens = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
                                                       wd["block_size"], wd["len_lo"], wd["len_hi"],
@@ -153,7 +164,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_causal", "bwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fwd_causal", "bwd", "prefill_paged", "decode", "copy"],
+                    default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -296,6 +308,20 @@ def main():
         f = acc.attention_flops(w4["B"], w4["H"], w4["N"], w4["d"], causal=True, seq_lens=lh)
         extras["gqa_varlen_8k_causal"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
                                           "seq_lens": lh}
+        # Chunked prefill against the paged cache (16 sequences, chunks of up to 1024 tokens).
+        from io_aware_attention_02_amd import fa_paged_prefill
+        from io_aware_attention_02_amd.inputs import paged_prefill_inputs
+        w5 = WORKLOADS["paged_prefill"]
+        pq, pkc, pvc, ptb, psl, pql = paged_prefill_inputs(
+            w5["S"], w5["Hq"], w5["Hkv"], w5["d"], w5["max_q"], w5["block_size"], w5["len_lo"],
+            w5["len_hi"], seed=w5["seed"])
+        f = acc.paged_prefill_flops(psl.tolist(), pql.tolist(), w5["Hq"], w5["d"])
+        pq, pkc, pvc, ptb, psl, pql = (t.to(dev) for t in (pq, pkc, pvc, ptb, psl, pql))
+        po = torch.empty_like(pq)
+        pl = torch.empty(pq.shape[:3], dtype=torch.float32, device=dev)
+        t = _time_calls(torch, lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql, po, pl), 10)
+        extras["paged_prefill"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2)}
+        del pkc, pvc
         # Backward (recompute from the forward's LSE) on the headline inputs, both masks.
         from io_aware_attention_02_amd import fa_bwd, fa_bwd_workspace_bytes
         from io_aware_attention_02_amd.inputs import output_gradient

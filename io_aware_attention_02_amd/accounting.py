@@ -4,6 +4,8 @@ The counts are the algorithmic ones the throughput figures are quoted in:
 * forward flops: two contractions of 2*N*N*d each per (batch, head), i.e. 4*B*H*N^2*d,
   halved under causal masking; with per-sequence lengths the sum over sequences of
   4*H*L_b^2*d (halved under causal).
+* chunked prefill flops: 4*Hq*d per visible (query, key) pair; the chunk of Q_b rows at offset
+  L_b - Q_b sees Q_b*(L_b - Q_b) + Q_b*(Q_b + 1)/2 pairs.
 * backward flops: five contractions of the same size (S = Q K^T recomputed, dV = P^T dO,
   dP = dO V^T, dQ = dS K, dK = dS^T Q), i.e. 2.5 times the forward's.
 * decode bytes: every cached K and V element a step must read (sum of L_b*Hkv*d*2 bytes for
@@ -20,6 +22,7 @@ import math
 __all__ = [
     "attention_flops",
     "attention_bwd_flops",
+    "paged_prefill_flops",
     "forward_min_bytes",
     "decode_bytes",
     "decode_flops",
@@ -46,6 +49,13 @@ def attention_flops(B, H, N, d, causal=False, seq_lens=None):
 def attention_bwd_flops(B, H, N, d, causal=False, seq_lens=None):
     """Algorithmic flops of one backward pass: five contractions, 2.5x the forward's."""
     return 2.5 * attention_flops(B, H, N, d, causal=causal, seq_lens=seq_lens)
+
+
+def paged_prefill_flops(seq_lens, q_lens, Hq, d):
+    """Algorithmic flops of one chunked prefill against the paged cache."""
+    pairs = sum(int(Q) * (int(L) - int(Q)) + int(Q) * (int(Q) + 1) // 2
+                for L, Q in zip(seq_lens, q_lens))
+    return 4 * Hq * d * pairs
 
 
 def forward_min_bytes(B, H, Hkv, N, d, elem_bytes=2):
