@@ -308,6 +308,21 @@ def main():
         f = acc.attention_flops(w4["B"], w4["H"], w4["N"], w4["d"], causal=True, seq_lens=lh)
         extras["gqa_varlen_8k_causal"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
                                           "seq_lens": lh}
+        # The standard unfused forward (S and P through device memory) on the 4K and 16K
+        # inputs: the baseline the pages compare fused attention against.
+        from io_aware_attention_02_amd import fa_fwd_unfused, fa_fwd_unfused_workspace_bytes
+        for name, (qq, kk, vv, ww, t_fused) in (
+                ("unfused_4k", (q2, k2, v2, w2, extras["prefill_4k"]["ms"])),
+                ("unfused_16k", (q, k, v, wf, t_pre))):
+            wsu = torch.empty(fa_fwd_unfused_workspace_bytes(ww["B"], ww["H"], ww["N"]),
+                              dtype=torch.uint8, device=dev)
+            ou = torch.empty_like(qq)
+            lu = torch.empty(qq.shape[:3], dtype=torch.float32, device=dev)
+            t = _time_calls(torch, lambda: fa_fwd_unfused(qq, kk, vv, ou, lu, workspace=wsu), 5)
+            f = acc.attention_flops(ww["B"], ww["H"], ww["N"], ww["d"])
+            extras[name] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
+                            "fused_speedup": round(t / t_fused, 2)}
+            del wsu
         # Chunked prefill against the paged cache (16 sequences, chunks of up to 1024 tokens).
         from io_aware_attention_02_amd import fa_paged_prefill
         from io_aware_attention_02_amd.inputs import paged_prefill_inputs

@@ -1,7 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) fused attention library (libfa.so).
  *
- * Four operations, all asynchronous on the caller's HIP stream:
+ * Five operations, all asynchronous on the caller's HIP stream:
  *
  *   fa_fwd           fused, tiled attention forward O = softmax(scale * Q K^T) V with an
  *                    online softmax; the N x N score and probability matrices never reach
@@ -11,6 +11,8 @@
  *   fa_paged_decode  one query token per sequence against a KV cache stored in fixed-size
  *                    physical blocks that a block table addresses (non-contiguous gather).
  *   fa_paged_prefill a chunk of each sequence's newest tokens against the same paged cache.
+ *   fa_fwd_unfused   the standard three-kernel forward (S and P through device memory), the
+ *                    baseline the fused kernel is measured against.
  *
  * Conventions for every entry point
  *   - Every data pointer is a caller-owned DEVICE pointer (e.g. from torch).  The library
@@ -189,6 +191,28 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
                            const int32_t* q_lens, void* o, float* lse, int num_seqs, int max_q,
                            int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
                            int num_blocks, float scale, void* stream);
+
+/*
+ * fa_fwd_unfused_workspace_bytes -- bytes of the workspace fa_fwd_unfused needs: the N x N
+ * score matrix in fp32 and the probability matrix in bf16 for every (batch, head).
+ */
+size_t fa_fwd_unfused_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_fwd_unfused -- the standard, unfused attention forward, kept as the baseline the fused
+ * kernel is measured against ("FlashAttention优化" §2.1-§2.2: S = scale * Q K^T written to
+ * device memory, a three-pass softmax reading S and writing P, then O = P V reading P).  Same
+ * result as fa_fwd (bf16, no padding lengths) at the cost of the N x N round trips.
+ *
+ *   q, k, v, o, lse, B, H, Hkv, d, scale, causal: as for fa_fwd (bf16 only).
+ *   N            a multiple of 8.
+ *   workspace    device buffer of at least fa_fwd_unfused_workspace_bytes(B, H, N) bytes,
+ *                16-byte aligned, owned by the caller (6 * B * H * N^2 bytes).
+ *   stream       hipStream_t or NULL.
+ */
+fa_status fa_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int N, int d, float scale, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* fa_status_str -- static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);

@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     fa_bwd,
     fa_bwd_workspace_bytes,
     fa_fwd,
+    fa_fwd_unfused,
+    fa_fwd_unfused_workspace_bytes,
     fa_paged_decode,
     fa_paged_decode_workspace_bytes,
     fa_paged_prefill,

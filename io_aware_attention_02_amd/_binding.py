@@ -19,6 +19,8 @@ __all__ = [
     "fa_bwd",
     "fa_bwd_workspace_bytes",
     "fa_fwd",
+    "fa_fwd_unfused",
+    "fa_fwd_unfused_workspace_bytes",
     "fa_paged_decode",
     "fa_paged_decode_workspace_bytes",
     "fa_paged_prefill",
@@ -71,6 +73,10 @@ def load_library():
     lib.fa_paged_prefill.restype = i32
     lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i32, f32, vp]
+    lib.fa_fwd_unfused_workspace_bytes.restype = sz
+    lib.fa_fwd_unfused_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.fa_fwd_unfused.restype = i32
+    lib.fa_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [i32]
     _LIB = lib
@@ -255,4 +261,39 @@ def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, q_lens, o=None,
                               d, bs, M, P, float(scale), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_paged_prefill")
+    return o, lse
+
+
+def fa_fwd_unfused_workspace_bytes(B, H, N):
+    return int(load_library().fa_fwd_unfused_workspace_bytes(int(B), int(H), int(N)))
+
+
+def fa_fwd_unfused(q, k, v, o=None, lse=None, scale=None, causal=False, workspace=None,
+                   stream=None):
+    """The standard three-kernel forward (baseline).  q [B,H,N,d], k/v [B,Hkv,N,d] bf16 with N a
+    multiple of 8.  Returns (o, lse) like fa_fwd.  ``workspace``: optional uint8 device tensor of
+    fa_fwd_unfused_workspace_bytes(B, H, N) bytes (allocated with torch if None)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t, torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B,H,N,d] and k, v [B,Hkv,N,d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty_like(q) if o is None else o
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_device_tensor("o", o, torch.bfloat16)
+    _check_device_tensor("lse", lse, torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_fwd_unfused_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_device_tensor("workspace", workspace)
+    st = lib.fa_fwd_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                            float(scale), int(bool(causal)), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_unfused")
     return o, lse

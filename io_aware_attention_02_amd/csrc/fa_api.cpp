@@ -72,6 +72,44 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fwd_unfused_workspace_bytes(int B, int H, int N) {
+  return fa::unfused_workspace_bytes(B, H, N);
+}
+
+fa_status fa_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int N, int d, float scale, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (N % 8 != 0) return FA_ERR_UNSUPPORTED;  // aligned 16-byte score and 8-byte P accesses
+  const long long tiles = (long long)B * H * ((N + 127) / 128);
+  const long long rows = (long long)B * H * N;
+  if (tiles > INT_MAX || rows / 4 + 1 > INT_MAX) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::unfused_workspace_bytes(B, H, N)) return FA_ERR_INVALID_ARG;
+  fa::UnfusedArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  const hipError_t e = fa::launch_fwd_unfused(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* q_lens, void* o, float* lse, int num_seqs, int max_q,

@@ -36,6 +36,21 @@ struct DecodeArgs {
   void* workspace;
 };
 
+struct UnfusedArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* workspace;  // S fp32 [B, H, N, N], then P bf16 [B, H, N, N]
+  int B, H, Hkv, N, d;
+  float scale;
+  bool causal;
+};
+
+size_t unfused_workspace_bytes(int B, int H, int N);
+hipError_t launch_fwd_unfused(const UnfusedArgs& a, hipStream_t stream);
+
 struct PagedPrefillArgs {
   const void* q;  // [S, Hq, max_q, d]
   const void* k_cache;

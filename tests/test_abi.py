@@ -32,7 +32,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_paged_decode",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_unfused",
+                                     "fa_fwd_unfused_workspace_bytes", "fa_paged_decode",
                                      "fa_paged_decode_workspace_bytes", "fa_paged_prefill",
                                      "fa_status_str"]
 
@@ -113,6 +114,31 @@ def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
+def test_unfused_workspace_bytes(lib):
+    # fp32 scores and bf16 probabilities: 6 bytes per (batch, head, query, key)
+    assert lib.fa_fwd_unfused_workspace_bytes(1, 8, 16384) == 6 * 8 * 16384 * 16384
+    assert lib.fa_fwd_unfused_workspace_bytes(0, 8, 16) == 0
+
+
+def _unf(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=8, Hkv=2, N=128, d=128, scale=0.1, causal=0, ws=P,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_unfused(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                              a["N"], a["d"], a["scale"], a["causal"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(ws=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=8, Hkv=3), INVALID), (dict(o=P + 4), INVALID),
+    (dict(scale=-2.0), INVALID), (dict(wsb=1000), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(N=100), UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 20, wsb=1 << 62), UNSUPPORTED),
+])
+def test_unfused_rejects(lib, kw, status):
+    assert _unf(lib, **kw) == status
+
+
 def _pre(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, sl=P, ql=P, o=P, lse=P, S=4, Q=64, Hq=32, Hkv=8, d=128, bs=16,
              M=64, nb=256, scale=0.1, stream=None)
@@ -166,6 +192,7 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     assert _dec(lib) == HIPERR
     assert _bwd(lib) == HIPERR
     assert _pre(lib) == HIPERR
+    assert _unf(lib) == HIPERR
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
