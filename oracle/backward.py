@@ -29,12 +29,16 @@ from .attention import _check_shapes, _lengths, _three_pass, _visible_keys
 __all__ = ["attention_bwd_ref"]
 
 
-def attention_bwd_ref(q, k, v, dout, scale, causal=False, seq_lens=None):
+def attention_bwd_ref(q, k, v, dout, scale, causal=False, seq_lens=None, rows=None):
     """Gradients (dQ [B,H,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d]) in float64.
 
     q, dout [B, H, N, d]; k, v [B, Hkv, N, d] (any real dtype; upcast exactly to float64).
-    scale, causal and seq_lens as for ``attention_ref``.
+    scale, causal and seq_lens as for ``attention_ref``.  With ``rows`` (a 1-D list of query
+    rows) only dQ of those rows is computed -- dQ_i needs row i of P alone -- and the result is
+    (dQ [B, H, n_rows, d], None, None).
     """
+    if rows is not None:
+        return _dq_rows(q, k, v, dout, scale, causal, seq_lens, rows), None, None
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -64,3 +68,30 @@ def attention_bwd_ref(q, k, v, dout, scale, causal=False, seq_lens=None):
             dq[b, h, :L] = scale * (ds @ kb)
             dk[b, g, :L] += scale * (ds.T @ qb)
     return dq, dk, dv
+
+
+def _dq_rows(q, k, v, dout, scale, causal, seq_lens, rows):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    B, H, Hkv, N, d = _check_shapes(q, k, v)
+    group = H // Hkv
+    lens = _lengths(seq_lens, B, N)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    dq = np.zeros((B, H, rows.size, d))
+    scale = float(scale)
+    for b in range(B):
+        L = lens[b]
+        valid = rows < L
+        if L == 0 or not valid.any():
+            continue
+        vr = rows[valid]
+        counts = _visible_keys(vr, L, causal)
+        for h in range(H):
+            g = h // group
+            _, _, p = _three_pass(q[b, h, vr], k[b, g, :L], v[b, g, :L], scale, counts)
+            dp = do[b, h, vr] @ v[b, g, :L].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, h, valid] = scale * (ds @ k[b, g, :L])
+    return dq

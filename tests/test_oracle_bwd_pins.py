@@ -133,3 +133,16 @@ def test_padding_is_inert():
     ref = attention_bwd_ref(q[:, :, :L], k[:, :, :L], v[:, :, :L], do[:, :, :L], 0.5, causal=True)
     for got, want in zip((dq, dk, dv), ref):
         np.testing.assert_allclose(got[:, :, :L], want, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, [7, 10])])
+def test_row_subset_equals_full_query_gradient(causal, lens):
+    rng = np.random.default_rng(29)
+    B, H, Hkv, N, d = 2, 4, 2, 10, 5
+    q, do = _rand(rng, B, H, N, d), _rand(rng, B, H, N, d)
+    k, v = _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, d)
+    full, _, _ = attention_bwd_ref(q, k, v, do, 0.3, causal=causal, seq_lens=lens)
+    rows = [9, 0, 4, 7]
+    sub, dk, dv = attention_bwd_ref(q, k, v, do, 0.3, causal=causal, seq_lens=lens, rows=rows)
+    assert dk is None and dv is None
+    np.testing.assert_allclose(sub, full[:, :, rows], rtol=0, atol=1e-13)
