@@ -87,8 +87,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int dtype, void* stream);
 
 /*
- * fa_bwd_workspace_bytes -- size in bytes of the device workspace fa_bwd needs (one fp32
- * per query row: D = rowsum(dO * O)).  Returns 0 for non-positive sizes.
+ * fa_bwd_workspace_bytes -- size in bytes of the device workspace fa_bwd needs: two fp32
+ * per query row, D = rowsum(dO * O) and the LSE in base 2, each array rounded up to 256 bytes.
+ * Returns 0 for non-positive sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 

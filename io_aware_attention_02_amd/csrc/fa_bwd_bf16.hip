@@ -9,16 +9,18 @@
 // (the derivative of the softmax, with D the row-wise dot product the softmax Jacobian needs).
 //
 // Three kernels, every one deterministic (no atomics):
-//  * bwd_pre_kernel   D_i = dO_i . O_i in fp32 for every row (0 for padding rows).
+//  * bwd_pre_kernel   D_i = dO_i . O_i in fp32 for every row (0 for padding rows) and the LSE in
+//                     base 2 (+inf for padding rows).
 //  * bwd_dq_kernel    query-stationary, laid out like the forward: a wave owns 32 query rows,
 //                     K and V tiles of 64 keys stream through LDS; S^T = K Q^T and dP^T = V dO^T
 //                     on the matrix cores, dS^T in registers, dQ^T += K^T dS^T with K^T read by
 //                     the transposing LDS read.
-//  * bwd_dkdv_kernel  key-stationary: a wave owns 32 keys (K, V in registers), query tiles of 64
-//                     rows of Q and dO (every query head of the kv head's group) stream through
-//                     LDS; S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
-//                     Summing the group's heads inside the kernel keeps grouped-query dK/dV free
-//                     of atomics.
+//  * bwd_dkdv_kernel  key-stationary: two waves own each 32 keys (K, V in registers), query tiles
+//                     of 64 rows of Q and dO (every query head of the kv head's group) stream
+//                     through LDS; one wave forms S = Q K^T, P and dV^T += dO^T P and passes P
+//                     through LDS to its partner, which forms dP = dO V^T, dS and
+//                     dK^T += Q^T dS.  Summing the group's heads inside the kernel keeps
+//                     grouped-query dK/dV free of atomics.
 // Every probability is rebuilt from the stored LSE as exp2(s * scale * log2 e - LSE * log2 e);
 // padding rows get LSE = +inf here so that their probabilities are exactly 0.
 #include "fa_device.h"
@@ -45,6 +47,7 @@ struct BwdParams {
   bf16* dk;
   bf16* dv;
   float* dvec;  // D [B, H, N]
+  float* lse2;  // LSE * log2 e [B, H, N] (+inf for padding rows)
   const int32_t* seq_lens;
   int B, H, group, Hkv, N, n_t, total;
   float scale, sl2;
@@ -81,12 +84,42 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && c == 0) p.dvec[row] = i < L ? acc : 0.f;
+  if (row < rows && c == 0) {
+    p.dvec[row] = i < L ? acc : 0.f;
+    p.lse2[row] = i < L ? p.lse[row] * kLog2e : kPosInf;
+  }
 }
 
-// Per-lane LDS byte offsets of the transposing reads of a tile stored with the K swizzle: for
-// 32-dim output block n, rows key and key + 8 of a 16-row chunk (the chunk base is added by
-// the caller as 16 * jj rows; the swizzle of row 16 jj + r equals that of row r).
+// Every tile of the backward is read as rows (the A operand of a score product) and, apart
+// from V in the dQ kernel, also transposed (the A operand of a gradient product), so all of
+// them are stored with the two-way swizzle Geo::swz_b.  Per-lane offsets of the direct loads:
+template <int D, int NW>
+__device__ __forceinline__ void tile_offsets_b(int* off, int wave, int lane) {
+  using G = Geo<D>;
+  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
+#pragma unroll
+  for (int t = 0; t < NI_W; ++t) {
+    const int row = (wave * NI_W + t) * G::RPI + lane / G::CPR;
+    off[t] = row * G::RB + (((lane % G::CPR) ^ G::swz_b(row)) << 4);
+  }
+}
+
+// Row reads: row lane & 31, logical chunk 2c + (lane >> 5) (the layout of FragAddr::k).
+template <int D>
+__device__ __forceinline__ FragAddr<D> frag_addr_b(int lane) {
+  using G = Geo<D>;
+  FragAddr<D> a;
+  const int c32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c) a.k[c] = c32 * G::RB + (((2 * c + hh) ^ G::swz_b(c32)) << 4);
+#pragma unroll
+  for (int n = 0; n < G::NB; ++n) a.v[n] = 0;  // unused
+  return a;
+}
+
+// Transposing reads: for 32-dim output block n, rows key and key + 8 of a 16-row chunk (the
+// chunk base is added by the caller as 16 * jj rows; the swizzle of row 16 jj + r equals that
+// of row r).
 template <int D>
 struct TrAddr {
   int lo[D / 32];
@@ -94,7 +127,7 @@ struct TrAddr {
 };
 
 template <int D>
-__device__ __forceinline__ TrAddr<D> tr_addr_k(int lane) {
+__device__ __forceinline__ TrAddr<D> tr_addr_b(int lane) {
   using G = Geo<D>;
   TrAddr<D> a;
   const int grp = lane >> 4, s = lane & 15;
@@ -102,13 +135,13 @@ __device__ __forceinline__ TrAddr<D> tr_addr_k(int lane) {
 #pragma unroll
   for (int n = 0; n < G::NB; ++n) {
     const int dim = n * 32 + 16 * (grp & 1) + 4 * (s & 3);
-    a.lo[n] = key * G::RB + (((dim >> 3) ^ G::swz_k(key)) << 4) + ((dim & 7) << 1);
-    a.hi[n] = (key + 8) * G::RB + (((dim >> 3) ^ G::swz_k(key + 8)) << 4) + ((dim & 7) << 1);
+    a.lo[n] = key * G::RB + (((dim >> 3) ^ G::swz_b(key)) << 4) + ((dim & 7) << 1);
+    a.hi[n] = (key + 8) * G::RB + (((dim >> 3) ^ G::swz_b(key + 8)) << 4) + ((dim & 7) << 1);
   }
   return a;
 }
 
-// A^T fragment (32 dims of block n x 16 rows of chunk jj) of a K-swizzled tile.
+// A^T fragment (32 dims of block n x 16 rows of chunk jj) of a tile.
 template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(const lds_t* tile, const TrAddr<D>& ta, int n, int jj) {
   using G = Geo<D>;
@@ -119,7 +152,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_t* tile, const TrAddr<D>& ta
 }
 
 // One 32-row block of a score product: s = rows[0..31] . bf over the head dimension (rows of a
-// K-swizzled tile, B operand in registers), reads kAheadK fragments ahead of their MFMAs.
+// tile, B operand in registers), reads kAheadK fragments ahead of their MFMAs.
 template <int D>
 __device__ __forceinline__ void scores_block(f32x16& s, const lds_t* rows, const FragAddr<D>& fa,
                                              const bf16x8 (&bf)[D / 16]) {
@@ -203,7 +236,7 @@ bwd_dq_kernel(BwdParams p) {
   const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
   const float sl2 = p.sl2;
   int off[NI_W];
-  tile_offsets<D, NW, false>(off, wave, lane);
+  tile_offsets_b<D, NW>(off, wave, lane);
   load_tile<D, NW>(K0, Kg, 0, L, off, wave);
   load_tile<D, NW>(V0, Vg, 0, L, off, wave);
 
@@ -220,8 +253,8 @@ bwd_dq_kernel(BwdParams p) {
   }
   const float lse2 = valid ? p.lse[(size_t)bh * N + qrow] * kLog2e : kPosInf;
   const float drow = valid ? p.dvec[(size_t)bh * N + qrow] : 0.f;
-  const FragAddr<D> fa = frag_addr<D>(lane);
-  const TrAddr<D> ta = tr_addr_k<D>(lane);
+  const FragAddr<D> fa = frag_addr_b<D>(lane);
+  const TrAddr<D> ta = tr_addr_b<D>(lane);
 
   f32x16 acc[G::NB];
 #pragma unroll
@@ -290,29 +323,60 @@ bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (batch, kv head, 128 keys); waves own 32 keys each.  The loop runs
-// over every query head of the group and every query tile of 64 rows that can see the keys.
+// dK, dV: one workgroup per (batch, kv head, 128 keys) of 8 waves.  Waves w and w + 4 share a
+// SIMD and own the same 32 keys.  Wave w (the P wave) holds K^T and the dV^T accumulator: it
+// forms S = Q K^T and P for 32 query rows, hands P (fp32, in the accumulator's lane order) to
+// its partner through LDS and adds dV^T += dO^T P.  Wave w + 4 (the dS wave) holds V^T and the
+// dK^T accumulator: it forms dP = dO V^T, takes P from LDS, dS = P o (dP - D) and adds
+// dK^T += Q^T dS.  Each wave thus holds one operand and one accumulator (about 170 registers),
+// two waves fit on a SIMD, and no product is computed twice.
+//
+// Query tiles of 64 rows (every query head of the group) are triple-buffered in LDS; each tile
+// is two halves of 32 rows with one workgroup barrier per half, which both publishes P and
+// orders buffer reuse:
+//   P wave:   S(h), P(h) -> LDS | barrier | dV(h), S(h+1), P(h+1) -> LDS | barrier | ...
+//   dS wave:  dP(h)             | barrier | dS(h), dK(h), dP(h+1)        | barrier | ...
+// After the first barrier of tile t every read of tile t-1 is done, so tile t+2 is loaded into
+// its buffer then; it must land before the second barrier of tile t+1.
+constexpr int kNWkv = 8;
+constexpr int kQBuf = 3;  // query tile buffers
+
+// Row statistics of a query tile (base-2 LSE or D, 64 fp32) straight into LDS, rows at or past
+// the valid length reading 0: with zero Q and dO rows there, P = 1 and dP = D = 0, so such
+// rows add exactly nothing to dK and dV.
+__device__ __forceinline__ void load_stats(lds_t* dst, const float* rowbase, int row0, int L,
+                                           int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int bytes = __builtin_amdgcn_readfirstlane(max(L - row0, 0) * 4);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(rowbase + row0);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, lane * 4, 0, 0, 0);
+#endif
+}
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64 * kNWb) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * kNWkv) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdParams p) {
   using G = Geo<D>;
-  constexpr int NW = kNWb;
-  constexpr int kBK = NW * kWQ;  // keys per workgroup
+  constexpr int NW = kNWkv;
+  constexpr int kBK = 4 * kWQ;  // keys per workgroup
   constexpr int NI_W = LoadGeo<D, NW>::NI_W;
-  __shared__ __attribute__((aligned(1024))) char q0s[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char q1s[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char o0s[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char o1s[G::TILE];
-  __shared__ __attribute__((aligned(16))) float lvec[2][kBN];  // LSE (base 2) of the tile rows
-  __shared__ __attribute__((aligned(16))) float dvec[2][kBN];  // D of the tile rows
-  lds_t* const Q0 = (lds_t*)q0s;
-  lds_t* const Q1 = (lds_t*)q1s;
-  lds_t* const O0 = (lds_t*)o0s;
-  lds_t* const O1 = (lds_t*)o1s;
+  constexpr int kLoadsPerTile = 2 * NI_W + 1;  // per wave: Q and dO tiles, one statistics row
+  __shared__ __attribute__((aligned(1024))) char qs[kQBuf][G::TILE];
+  __shared__ __attribute__((aligned(1024))) char os[kQBuf][G::TILE];
+  __shared__ __attribute__((aligned(16))) float lvec[kQBuf][kBN];  // LSE (base 2) of the rows
+  __shared__ __attribute__((aligned(16))) float dvec[kQBuf][kBN];  // D of the rows
+  // P in fp32, as the dS wave needs it: [half][slice][chunk][rows 0-3 / 8-11 of the chunk][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 pex[2][4][2][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, hh = lane >> 5;
+  const int role = __builtin_amdgcn_readfirstlane(wave >> 2);  // 0: P wave, 1: dS wave
+  const int slice = wave & 3;
   int unit, kt;
   unit_of(p, p.n_t, unit, kt);
   const int b = unit / p.Hkv, g = unit - b * p.Hkv;
@@ -330,20 +394,21 @@ bwd_dkdv_kernel(BwdParams p) {
     }
     return;
   }
-  const bf16* Kg = p.k + (size_t)(b * p.Hkv + g) * N * D;
-  const bf16* Vg = p.v + (size_t)(b * p.Hkv + g) * N * D;
-  const int kw0 = k0 + wave * kWQ;
+  const int kw0 = k0 + slice * kWQ;
   const int key = kw0 + c32;  // this lane's key column
   const float sl2 = p.sl2;
 
-  // K^T and V^T fragments (B operands of S = Q K^T and dP = dO V^T), zero past the length.
-  bf16x8 kf[G::KC], vf[G::KC];
+  // K^T (P wave) or V^T (dS wave) fragments: the B operand of S = Q K^T or dP = dO V^T, zero
+  // past the length.
+  bf16x8 bf[G::KC];
+  {
+    const bf16* src = (role == 0 ? p.k : p.v) + (size_t)(b * p.Hkv + g) * N * D;
 #pragma unroll
-  for (int c = 0; c < G::KC; ++c) {
-    const size_t at = (size_t)key * D + c * 16 + hh * 8;
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    kf[c] = key < L ? *reinterpret_cast<const bf16x8*>(Kg + at) : zero;
-    vf[c] = key < L ? *reinterpret_cast<const bf16x8*>(Vg + at) : zero;
+    for (int c = 0; c < G::KC; ++c) {
+      const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      bf[c] = key < L ? *reinterpret_cast<const bf16x8*>(src + (size_t)key * D + c * 16 + hh * 8)
+                      : zero;
+    }
   }
 
   // Query tiles: causal rows before the workgroup's first key never see it.
@@ -351,132 +416,139 @@ bwd_dkdv_kernel(BwdParams p) {
   const int n_q = (L + kBN - 1) / kBN - qt0;
   const int n_it = p.group * n_q;
   int off[NI_W];
-  tile_offsets<D, NW, false>(off, wave, lane);
-  const FragAddr<D> fa = frag_addr<D>(lane);
-  const TrAddr<D> ta = tr_addr_k<D>(lane);
-  // Iteration it -> (query head of the group, query tile).
-  auto head_of = [&](int it) __attribute__((always_inline)) { return g * p.group + it / n_q; };
-  auto qrow0 = [&](int it) __attribute__((always_inline)) { return (qt0 + it % n_q) * kBN; };
-  // Row statistics of a tile: each wave fills 16 of the 64 entries (+inf / 0 past the length).
-  float l_next = kPosInf, d_next = 0.f;
-  auto fetch_stats = [&](int it) __attribute__((always_inline)) {
-    const int r = qrow0(it) + wave * 16 + (lane & 15);
-    const size_t at = ((size_t)b * p.H + head_of(it)) * N + r;
-    const bool ok = lane < 16 && r < L;
-    l_next = ok ? p.lse[at] * kLog2e : kPosInf;
-    d_next = ok ? p.dvec[at] : 0.f;
-  };
-  auto store_stats = [&](int buf) __attribute__((always_inline)) {
-    if (lane < 16) {
-      lvec[buf][wave * 16 + lane] = l_next;
-      dvec[buf][wave * 16 + lane] = d_next;
-    }
-  };
-  auto load_q = [&](int it, lds_t* Qd, lds_t* Od) __attribute__((always_inline)) {
-    const size_t hb = ((size_t)b * p.H + head_of(it)) * N * D;
-    load_tile<D, NW>(Qd, p.q + hb, qrow0(it), L, off, wave);
-    load_tile<D, NW>(Od, p.dout + hb, qrow0(it), L, off, wave);
+  tile_offsets_b<D, NW>(off, wave, lane);
+  const FragAddr<D> fa = frag_addr_b<D>(lane);
+  const TrAddr<D> ta = tr_addr_b<D>(lane);
+  // Odd waves fetch the LSE row, even waves D (redundantly, so that every wave issues the same
+  // number of loads per tile and one vmcnt value waits for a tile).
+  const float* stat_src = (wave & 1) ? p.lse2 : p.dvec;
+  auto issue = [&](int it, int buf) __attribute__((always_inline)) {
+    const int hq = g * p.group + it / n_q;
+    const int r0 = (qt0 + it % n_q) * kBN;
+    const size_t hb = ((size_t)b * p.H + hq) * N;
+    load_tile<D, NW>((lds_t*)qs[buf], p.q + hb * D, r0, L, off, wave);
+    load_tile<D, NW>((lds_t*)os[buf], p.dout + hb * D, r0, L, off, wave);
+    load_stats((wave & 1) ? (lds_t*)lvec[buf] : (lds_t*)dvec[buf], stat_src + hb, r0, L, lane);
   };
 
-  f32x16 dk[G::NB], dv[G::NB];
+  f32x16 acc[G::NB];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int n = 0; n < G::NB; ++n) dk[n] = dv[n] = f32x16{};
+  for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
 
-  // One LDS tile of 64 query rows, in two halves of 32: S = Q K^T and dP = dO V^T for the
-  // half (rows = queries, lane column = key), then per 16-row chunk P and dS and the dV^T, dK^T
-  // updates.  Working in halves keeps only one score block of each product live.
-  auto tile = [&](const lds_t* Qc, const lds_t* Oc, int buf, int q0t, auto masked) __attribute__((always_inline)) {
+  // Half hq of the tile in buffer buf, first stage (before the barrier): the P wave forms S and
+  // P for rows 32 hq .. 32 hq + 31 and publishes P; the dS wave forms dP.
+  auto stage1 = [&](int buf, int q0t, int hq, bf16x8 (&pf)[2], f32x16& sx, auto masked, auto rl) __attribute__((always_inline)) {
     constexpr bool M = decltype(masked)::value;
-#pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      f32x16 sS, sP;
-      scores_block<D>(sS, Qc + hq * 32 * G::RB, fa, kf);
-      scores_block<D>(sP, Oc + hq * 32 * G::RB, fa, vf);
+    constexpr int R = decltype(rl)::value;
+    const lds_t* rows = (const lds_t*)(R == 0 ? qs[buf] : os[buf]) + hq * 32 * G::RB;
+    scores_block<D>(sx, rows, fa, bf);
+    if constexpr (R == 0) {
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2) {
         const int jj = 2 * hq + j2;
         // Rows of chunk jj held by this lane: 16 jj + 4 hh + {0..3} and 16 jj + 8 + 4 hh + {0..3}.
         const f32x4 la = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 4 * hh]);
         const f32x4 lb = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 8 + 4 * hh]);
-        const f32x4 da = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 4 * hh]);
-        const f32x4 db = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 8 + 4 * hh]);
-        float pe[8], de[8];
+        float e[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const float x = sS[8 * j2 + t];
-          const float l2 = t < 4 ? la[t & 3] : lb[t & 3];
-          const float dd = t < 4 ? da[t & 3] : db[t & 3];
-          float arg = fmaf(x, sl2, -l2);
+          float arg = fmaf(sx[8 * j2 + t], sl2, -(t < 4 ? la[t & 3] : lb[t & 3]));
           if constexpr (M) {
             const int qr = q0t + 16 * jj + 8 * (t >> 2) + 4 * hh + (t & 3);
             if (key >= L || (CAUSAL && key > qr)) arg = kNegInf;
           }
-          pe[t] = fast_exp2(arg);
-          de[t] = pe[t] * (sP[8 * j2 + t] - dd);
+          e[t] = fast_exp2(arg);
         }
-        const bf16x8 pf = pack_bf16x8(pe);
-        const bf16x8 dsf = pack_bf16x8(de);
-#pragma unroll
-        for (int n = 0; n < G::NB; ++n) {
-          dv[n] = mfma32(tr_frag<D>(Oc, ta, n, jj), pf, dv[n]);
-          dk[n] = mfma32(tr_frag<D>(Qc, ta, n, jj), dsf, dk[n]);
-        }
+        pf[j2] = pack_bf16x8(e);
+        pex[hq][slice][j2][0][lane] = f32x4{e[0], e[1], e[2], e[3]};
+        pex[hq][slice][j2][1][lane] = f32x4{e[4], e[5], e[6], e[7]};
       }
     }
   };
-  // A tile needs the mask when it straddles the causal diagonal of this workgroup's keys or
-  // when some of those keys lie past the valid length; a wave whose keys all come after the
-  // tile's last row skips it.
-  auto iter = [&](int it, auto parity) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(parity)::value;
-    lds_t* const Qc = ODD ? Q1 : Q0;
-    lds_t* const Oc = ODD ? O1 : O0;
-    lds_t* const Qn = ODD ? Q0 : Q1;
-    lds_t* const On = ODD ? O0 : O1;
-    constexpr int BUF = ODD ? 1 : 0;
-    if (it + 1 < n_it) {
-      load_q(it + 1, Qn, On);
-      fetch_stats(it + 1);
+  // Second stage (after the barrier): dV^T += dO^T P, or dS and dK^T += Q^T dS.
+  auto stage2 = [&](int buf, int hq, const bf16x8 (&pf)[2], const f32x16& sx, auto rl) __attribute__((always_inline)) {
+    constexpr int R = decltype(rl)::value;
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const int jj = 2 * hq + j2;
+      bf16x8 opnd;
+      if constexpr (R == 0) {
+        opnd = pf[j2];
+      } else {
+        const f32x4 pa = pex[hq][slice][j2][0][lane];
+        const f32x4 pb = pex[hq][slice][j2][1][lane];
+        const f32x4 da = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 4 * hh]);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 8 + 4 * hh]);
+        float e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float pv = t < 4 ? pa[t & 3] : pb[t & 3];
+          e[t] = pv * (sx[8 * j2 + t] - (t < 4 ? da[t & 3] : db[t & 3]));
+        }
+        opnd = pack_bf16x8(e);
+      }
+      const lds_t* tr = (const lds_t*)(R == 0 ? os[buf] : qs[buf]);
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) acc[n] = mfma32(tr_frag<D>(tr, ta, n, jj), opnd, acc[n]);
     }
-    const int q0t = qrow0(it);
-    const bool masked = (CAUSAL && q0t < k0 + kBK - 1) || k0 + kBK > L;
-    if (!CAUSAL || q0t + kBN - 1 >= kw0) {
-      if (masked) tile(Qc, Oc, BUF, q0t, std::true_type{});
-      else tile(Qc, Oc, BUF, q0t, std::false_type{});
-    }
-    if (it + 1 < n_it) store_stats(1 - BUF);
-    wait_loads();
-    __syncthreads();
   };
-  load_q(0, Q0, O0);
-  fetch_stats(0);
-  store_stats(0);
-  wait_loads();
-  __syncthreads();
-  int it = 0;
-  for (; it + 1 < n_it; it += 2) {
-    iter(it, std::false_type{});
-    iter(it + 1, std::true_type{});
-  }
-  if (it < n_it) iter(it, std::false_type{});
+
+  // Both roles run the same barrier sequence; a wave whose keys all come after a tile's last row
+  // (causal) skips the tile's arithmetic but not its barriers or loads.
+  auto run = [&](auto rl) __attribute__((always_inline)) {
+    issue(0, 0);
+    if (n_it > 1) issue(1, 1);
+    if (n_it > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoadsPerTile));
+    else wait_loads();
+    __syncthreads();
+    int buf = 0;
+    for (int it = 0; it < n_it; ++it) {
+      const int q0t = (qt0 + it % n_q) * kBN;
+      const bool masked = (CAUSAL && q0t < k0 + kBK - 1) || k0 + kBK > L;
+      const bool active = !CAUSAL || q0t + kBN - 1 >= kw0;
+      const int buf2 = buf == 0 ? 2 : buf - 1;  // (buf + 2) % 3
+      bf16x8 pf[2];
+      f32x16 sx;
+      auto half = [&](int hq) __attribute__((always_inline)) {
+        if (active) {
+          if (masked) stage1(buf, q0t, hq, pf, sx, std::true_type{}, rl);
+          else stage1(buf, q0t, hq, pf, sx, std::false_type{}, rl);
+        }
+        if (hq == 1) {  // tile it + 1 (issued a tile ago) must have landed
+          if (it + 2 < n_it) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoadsPerTile));
+          else wait_loads();
+        }
+        __syncthreads();
+        if (hq == 0 && it + 2 < n_it) issue(it + 2, buf2);
+        if (active) stage2(buf, hq, pf, sx, rl);
+      };
+      half(0);
+      half(1);
+      buf = buf == 2 ? 0 : buf + 1;
+    }
+  };
+  if (role == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 
   if (key < N) {
+    bf16* out = role == 0 ? dVg : dKg;
+    const float f = role == 0 ? 1.f : p.scale;
 #pragma unroll
     for (int n = 0; n < G::NB; ++n) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk[n][4 * r4 + 0] * p.scale, dk[n][4 * r4 + 1] * p.scale);
-        wk[1] = pack_bf16x2(dk[n][4 * r4 + 2] * p.scale, dk[n][4 * r4 + 3] * p.scale);
-        wv[0] = pack_bf16x2(dv[n][4 * r4 + 0], dv[n][4 * r4 + 1]);
-        wv[1] = pack_bf16x2(dv[n][4 * r4 + 2], dv[n][4 * r4 + 3]);
-        const size_t at = (size_t)key * D + n * 32 + 8 * r4 + 4 * hh;
-        *reinterpret_cast<u32x2*>(dKg + at) = wk;
-        *reinterpret_cast<u32x2*>(dVg + at) = wv;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[n][4 * r4 + 0] * f, acc[n][4 * r4 + 1] * f);
+        w[1] = pack_bf16x2(acc[n][4 * r4 + 2] * f, acc[n][4 * r4 + 3] * f);
+        *reinterpret_cast<u32x2*>(out + (size_t)key * D + n * 32 + 8 * r4 + 4 * hh) = w;
       }
     }
   }
 }
+
+// Floats in one per-row statistics array (D or the base-2 LSE) of the workspace, rounded up to
+// 256 bytes.
+size_t stat_floats(int B, int H, int N) { return ((size_t)B * H * N + 63) / 64 * 64; }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
@@ -491,6 +563,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   p.dk = static_cast<bf16*>(a.dk);
   p.dv = static_cast<bf16*>(a.dv);
   p.dvec = static_cast<float*>(a.workspace);
+  p.lse2 = p.dvec + stat_floats(a.B, a.H, a.N);
   p.seq_lens = a.seq_lens;
   p.B = a.B;
   p.H = a.H;
@@ -505,7 +578,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
                      stream, p);
   p.n_t = (a.N + kNWb * kWQ - 1) / (kNWb * kWQ);
   p.total = a.B * a.Hkv * p.n_t;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total), dim3(64 * kNWb), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total), dim3(64 * kNWkv), 0, stream, p);
   p.total = a.B * a.H * p.n_t;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total), dim3(64 * kNWb), 0, stream, p);
   return hipGetLastError();
@@ -515,7 +588,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
 
 size_t bwd_workspace_bytes(int B, int H, int N) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return ((size_t)B * H * N * sizeof(float) + 255) / 256 * 256;
+  return 2 * stat_floats(B, H, N) * sizeof(float);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {

@@ -35,6 +35,14 @@ struct Geo {
   // transposing read touches cover every bank group exactly twice.
   __device__ static int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
   __device__ static int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+  // Both ways (a tile read as rows and transposed): the K swizzle's row bits with the two 2-bit
+  // halves exchanged.  16 consecutive rows still map to 16 distinct bank groups, and the 4
+  // rows of one transposing read land in 4 different groups of 4 (the K swizzle puts them in
+  // the same 4 groups: a 4-way conflict).
+  __device__ static int swz_b(int row) {
+    const int m = D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D == 128 ? ((m & 3) << 2) | (m >> 2) : ((m & 1) << 2) | (m >> 1);
+  }
 };
 
 // Direct tile loads per wave for a workgroup of NW waves.
@@ -85,6 +93,10 @@ __device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0
 __device__ __forceinline__ void wait_loads() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); lgkm and exp counters untouched
 }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+// (vmcnt in bits 3:0 and 15:14), leaving the other counters untouched.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
 // Per-lane LDS byte offsets of the fragment reads, fixed for the whole kernel.
 template <int D>

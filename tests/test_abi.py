@@ -83,9 +83,9 @@ def test_fwd_rejects(lib, kw, status):
 
 
 def test_bwd_workspace_bytes(lib):
-    # one fp32 per query row, rounded up to 256 bytes
-    assert lib.fa_bwd_workspace_bytes(1, 8, 16384) == 8 * 16384 * 4
-    assert lib.fa_bwd_workspace_bytes(1, 1, 3) == 256
+    # two fp32 per query row (D and the base-2 LSE), each array rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_bytes(1, 8, 16384) == 2 * 8 * 16384 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3) == 512
     assert lib.fa_bwd_workspace_bytes(0, 8, 16) == 0
     assert lib.fa_bwd_workspace_bytes(2, 8, -1) == 0
 
