@@ -1,0 +1,127 @@
+"""FP8 (e4m3) attention forward in float64 (oracle; test infrastructure).
+
+The pages name FP8 as the main addition of FlashAttention V3 (the "GPU优化" tag page,
+guijiagi.com, excerpt "注意力计算的性能瓶颈", part Flash Attention V3: FP8 tensor cores and an
+asynchronous pipeline on the H100) without fixing the arithmetic.  The reading taken here
+(listed in the design doc):
+
+* Inputs are FP8 e4m3 codes (the OCP "fn" variant: 4 exponent bits with bias 7, 3 mantissa
+  bits, no infinities, max 448) with one float descale factor per tensor: the real value of a
+  code c of Q is ``q_scale * e4m3(c)`` (likewise K, V).
+* The attention computed is the one of the dequantised tensors, O = softmax(scale * Q K^T) V,
+  with the online softmax of "FlashAttention优化" (coreui.cn) §3.2.1: the keys are visited in
+  blocks of ``block`` keys, a running row maximum m and sum l are kept, and the accumulated
+  output and sum are rescaled by exp(m_old - m_new) whenever the maximum grows.
+* The probabilities of a block, p = exp(s - m_new) in (0, 1], enter the P V product as FP8:
+  ``e4m3_round(p_scale * p) / p_scale`` (p_scale = 256 spends the e4m3 range above 1 on keeping
+  small probabilities out of the subnormals).  The row sum l uses the unrounded p, so the LSE
+  is the exact log-sum-exp of the scaled scores.
+
+Because the rounding of p happens relative to the running maximum of each block, the result
+depends on the block size; ``block`` must equal the fused kernel's key tile (128).  With
+``p_scale=None`` nothing is rounded and the function is the exact attention of the dequantised
+inputs (pinned against the three-pass oracle).
+
+e4m3 decoding and rounding are written out from the format's definition (no library cast).
+"""
+
+import numpy as np
+
+from .attention import _check_shapes, _lengths, _visible_keys
+
+__all__ = ["e4m3_decode", "e4m3_round", "attention_fp8_ref", "E4M3_MAX"]
+
+E4M3_MAX = 448.0
+_BIAS = 7
+_MAN = 3
+
+
+def e4m3_decode(codes):
+    """Float64 values of e4m3fn byte codes (NaN for the two NaN codes 0x7f and 0xff)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> _MAN) & 0xF
+    m = c & 0x7
+    normal = sign * np.ldexp(1.0 + m / 8.0, e - _BIAS)
+    sub = sign * np.ldexp(m / 8.0, 1 - _BIAS)          # exponent field 0: m/8 * 2^-6
+    out = np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e4m3_round(x):
+    """Round float64 values to the nearest e4m3fn value, ties to the even mantissa.
+
+    |x| must not exceed the largest finite value (448) by half a unit or more (no saturation
+    is needed on the paths that use it: probabilities times 256 stay <= 256).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    if np.any(ax >= E4M3_MAX + 16.0):  # 448 + half of the top spacing (32)
+        raise ValueError("value outside the e4m3 range")
+    # spacing of representable values around ax: 2^(e - 3) for normals (ax >= 2^-6), 2^-9 below
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, 1 - _BIAS)
+    q = np.ldexp(1.0, (e - _MAN).astype(np.int64))
+    n = ax / q
+    r = np.floor(n)
+    frac = n - r
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2) == 1))
+    r = r + up
+    return np.sign(x) * r * q
+
+
+def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False, seq_lens=None,
+                      block=128, p_scale=256.0):
+    """FP8 attention forward: (O [B, H, N, d], LSE [B, H, N]) in float64.
+
+    q8 [B, H, N, d], k8 and v8 [B, Hkv, N, d]: e4m3 byte codes (uint8).  q_scale, k_scale,
+    v_scale: per-tensor descale factors.  scale: the softmax scale of the scores.  causal,
+    seq_lens, grouped-query heads and padding as for ``attention_ref``.  block: keys per block of
+    the online softmax.  p_scale: the factor applied before rounding probabilities to e4m3, or
+    None for no rounding.
+    """
+    q = e4m3_decode(q8) * float(q_scale)
+    k = e4m3_decode(k8) * float(k_scale)
+    v = e4m3_decode(v8) * float(v_scale)
+    B, H, Hkv, N, d = _check_shapes(q, k, v)
+    group = H // Hkv
+    lens = _lengths(seq_lens, B, N)
+    o = np.zeros((B, H, N, d))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        L = lens[b]
+        if L == 0:
+            continue
+        counts = _visible_keys(np.arange(L), L, causal)
+        for h in range(H):
+            g = h // group
+            ob, lb = _online(q[b, h, :L], k[b, g, :L], v[b, g, :L], float(scale), counts, block,
+                             p_scale)
+            o[b, h, :L] = ob
+            lse[b, h, :L] = lb
+    return o, lse
+
+
+def _online(qb, kb, vb, scale, counts, block, p_scale):
+    """Online softmax over key blocks for the rows of one sequence (every row sees >= 1 key)."""
+    n, L = qb.shape[0], kb.shape[0]
+    s = scale * (qb @ kb.T)
+    s = np.where(np.arange(L)[None, :] >= counts[:, None], -np.inf, s)
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, vb.shape[1]))
+    for j0 in range(0, L, block):
+        sj = s[:, j0:j0 + block]
+        bm = sj.max(axis=1)
+        m_new = np.maximum(m, bm)
+        # rows with no visible key so far keep m = -inf and add nothing
+        seen = m_new > -np.inf
+        ref = np.where(seen, m_new, 0.0)
+        alpha = np.where(seen, np.exp(np.where(seen, m - ref, 0.0)), 1.0)
+        p = np.exp(sj - ref[:, None])                      # 0 where masked
+        l = alpha * l + p.sum(axis=1)
+        pq = p if p_scale is None else e4m3_round(p_scale * p) / p_scale
+        acc = alpha[:, None] * acc + pq @ vb[j0:j0 + block]
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
