@@ -1,11 +1,13 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) fused attention library (libfa.so).
  *
- * Five operations, all asynchronous on the caller's HIP stream:
+ * Six operations, all asynchronous on the caller's HIP stream:
  *
  *   fa_fwd           fused, tiled attention forward O = softmax(scale * Q K^T) V with an
  *                    online softmax; the N x N score and probability matrices never reach
  *                    device memory.  Also writes the per-row log-sum-exp.
+ *   fa_fwd_fp8       the same forward with FP8 (e4m3) q, k, v and per-tensor scales, both
+ *                    products on the FP8 matrix cores.
  *   fa_bwd           the matching backward (dQ, dK, dV), recomputing the probabilities from
  *                    the stored log-sum-exp.
  *   fa_paged_decode  one query token per sequence against a KV cache stored in fixed-size
@@ -85,6 +87,32 @@ enum { FA_BF16 = 0, /* bf16 storage, fp32 arithmetic and accumulation on the mat
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int Hkv, int N, int d, float scale, int causal, const int32_t* seq_lens,
                  int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward from FP8 inputs.
+ *
+ * The FP8 variant of fa_fwd (FP8 tensor-core attention is what the "GPU优化" tag page,
+ * excerpt "注意力计算的性能瓶颈", credits FlashAttention V3 with).  q, k, v hold e4m3 codes
+ * (OCP e4m3fn: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, largest
+ * finite value 448); the tensor they stand for is the descale factor times the decoded codes,
+ * Q = q_scale * e4m3(q) and likewise K, V.  Computes O = softmax(scale * Q K^T) V and the LSE
+ * as fa_fwd does, with these differences in arithmetic:
+ *   - both products run on the FP8 matrix cores with fp32 accumulation;
+ *   - the softmax runs over blocks of 64 keys with a running row maximum m (the online
+ *     recurrence of "FlashAttention优化" §3.2.1); the probabilities exp(S - m) of a block enter
+ *     the P V product rounded to e4m3 after a factor 256 (relative error at most 2^-4 each),
+ *     while the row sum and the LSE use them unrounded.
+ *
+ *   q         [B, H, N, d] e4m3 codes (1 byte each)
+ *   k, v      [B, Hkv, N, d] e4m3 codes
+ *   q_scale, k_scale, v_scale  descale factors, finite and >= 0
+ *   o         [B, H, N, d] bf16, written (0 for padding rows)
+ *   lse       [B, H, N] fp32, written, as for fa_fwd (-inf for padding rows)
+ *   B, H, Hkv, N, d, scale, causal, seq_lens, stream: as for fa_fwd (d: 64 or 128).
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                     float v_scale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+                     float scale, int causal, const int32_t* seq_lens, void* stream);
 
 /*
  * fa_bwd_workspace_bytes -- size in bytes of the device workspace fa_bwd needs: two fp32

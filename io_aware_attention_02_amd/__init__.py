@@ -1,5 +1,5 @@
-"""Fused attention forward, its recompute backward, paged decode and chunked prefill against
-the paged cache, for AMD Instinct MI355X (gfx950).
+"""Fused attention forward (bf16, fp32 and FP8 inputs), its recompute backward, paged decode and
+chunked prefill against the paged cache, for AMD Instinct MI355X (gfx950).
 
 The compute runs in hand-written HIP kernels behind a small C ABI (``include/fa.h``,
 built as ``libfa.so`` next to this file).  This package is the thin Python binding over it:
@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     fa_bwd,
     fa_bwd_workspace_bytes,
     fa_fwd,
+    fa_fwd_fp8,
     fa_fwd_unfused,
     fa_fwd_unfused_workspace_bytes,
     fa_paged_decode,

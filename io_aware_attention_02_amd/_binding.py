@@ -18,6 +18,7 @@ __all__ = [
     "FaError",
     "fa_bwd",
     "fa_bwd_workspace_bytes",
+    "fa_fwd_fp8",
     "fa_fwd",
     "fa_fwd_unfused",
     "fa_fwd_unfused_workspace_bytes",
@@ -60,6 +61,9 @@ def load_library():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.restype = i32
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp]
+    lib.fa_fwd_fp8.restype = i32
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f32, f32, f32, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                               vp, vp]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
     lib.fa_bwd.restype = i32
@@ -139,6 +143,43 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, seq_lens=None, s
                     int(bool(causal)), _ptr(seq_lens), dtype, _stream(stream))
     if st != 0:
         raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o=None, lse=None, scale=None, causal=False,
+               seq_lens=None, stream=None):
+    """FP8 attention forward.  q [B,H,N,d], k/v [B,Hkv,N,d]: e4m3 codes (uint8 or
+    torch.float8_e4m3fn tensors); the real tensors are ``q_scale * q`` etc.
+
+    Returns (o, lse): o [B,H,N,d] bf16, lse [B,H,N] fp32.  ``scale`` defaults to 1/sqrt(d).
+    """
+    lib = load_library()
+    codes = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        _check_device_tensor(name, t, torch.uint8)
+        codes.append(t)
+    q, k, v = codes
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B,H,N,d] and k, v [B,Hkv,N,d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_device_tensor("o", o, torch.bfloat16)
+    _check_device_tensor("lse", lse, torch.float32)
+    if seq_lens is not None:
+        _check_device_tensor("seq_lens", seq_lens, torch.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), float(q_scale), float(k_scale), float(v_scale),
+                        _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                        _ptr(seq_lens), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_fp8")
     return o, lse
 
 

@@ -72,6 +72,42 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                     float v_scale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+                     float scale, int causal, const int32_t* seq_lens, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale) || !valid_scale(q_scale) || !valid_scale(k_scale) ||
+      !valid_scale(v_scale))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long long tiles = (long long)B * H * ((N + 127) / 128);
+  if (tiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+  fa::Fp8FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.o = o;
+  a.lse = lse;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_fwd_unfused_workspace_bytes(int B, int H, int N) {
   return fa::unfused_workspace_bytes(B, H, N);
 }

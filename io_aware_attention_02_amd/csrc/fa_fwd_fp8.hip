@@ -1,0 +1,424 @@
+// fa_fwd_fp8.hip -- fused attention forward with FP8 (e4m3) Q, K, V on the gfx950 FP8 MFMA.
+//
+// The FP8 variant of the fused forward: Q, K and V arrive as e4m3 codes with one descale
+// factor per tensor (the FP8 tensor-core attention the "GPU优化" tag page attributes to
+// FlashAttention V3, excerpt "注意力计算的性能瓶颈").  Both products run on
+// v_mfma_f32_32x32x64_f8f6f4 (64-deep contraction, fp32 accumulation): the scores S^T = K Q^T
+// from the codes (the descale factors fold into the softmax scale), and O^T += V^T P^T with the
+// probabilities rounded to e4m3.  The softmax is the online recurrence of "FlashAttention优化"
+// §3.2.1 over blocks of 64 keys: the probabilities of a block are relative to the running
+// maximum, exp(s - m) <= 1, and are multiplied by 256 before the rounding so that small values
+// stay out of the e4m3 subnormals; the row sum uses them unrounded, and the output is
+// multiplied by v_scale / sum at the end.  The output and sum are rescaled only when some row's
+// maximum grew (after the first blocks, rarely).
+//
+// CDNA4 mapping:
+//  * A wave owns 32 query rows, an LDS tile is 128 keys (two softmax blocks); workgroups of 8
+//    waves (256 rows, one per CU) or 4 waves (128 rows) as in the bf16 forward.  K and V tiles
+//    (128 x d bytes) go from global memory straight into LDS (buffer_load ... lds),
+//    double-buffered, one barrier per tile.
+//  * Operand layout of the FP8 MFMA (measured): lane l holds row l & 31 of A and column l & 31
+//    of B, 32 bytes each; byte j of the lanes l >> 5 = h is the same contraction slot in A and
+//    B.  Scores: A = K rows (32 keys), B = Q rows in registers, slot (h, j) = dimension
+//    64 c + 32 h + j.  The accumulator holds one query per lane and, of a 32-key block, keys
+//    8 (r >> 2) + 4 h + (r & 3) for r = 0..15.
+//  * P V: the probabilities of two 32-key blocks, converted to e4m3 in accumulator order, are
+//    directly the B operand (slot (h, j) = key 32 (j >> 4) + 8 ((j & 15) >> 2) + 4 h + (j & 3)).
+//    The A operand V^T (32 dims x the same 64 keys) comes from ds_read_b64_tr_b8, the 8-bit
+//    transposing LDS read: within each 16-lane group, output lane s gets byte s & 7 of the
+//    8-byte row piece addressed by lane 2 b + (s >> 3), for b = 0..7.  Four such reads fill one
+//    operand.
+//  * The 16-byte chunks of the K and V rows in LDS are XOR-swizzled by key so that the row
+//    reads (K) and the transposing reads (V) are free of bank conflicts.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+#include <type_traits>
+
+namespace fa {
+namespace {
+
+typedef __attribute__((address_space(3))) char lds8_t;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int kCUs8 = 256;
+constexpr int kXcds8 = 8;
+constexpr int kWQ8 = 32;               // query rows per wave
+constexpr int kBN8 = 128;              // keys per tile
+constexpr int kPScaleLog2 = 8;         // probabilities are rounded to e4m3 as 256 p
+constexpr int kBufFlags8 = 0x00020000; // buffer resource word 3: 32-bit data format, raw
+constexpr int kSchedMfma8 = 0x008;     // instruction-group masks of sched_group_barrier
+constexpr int kSchedDsRead8 = 0x100;
+constexpr int kAhead8 = 2;             // score MFMAs whose K reads are in flight
+constexpr int kAheadV8 = 2;            // P V MFMAs whose V reads are in flight
+
+template <int D>
+struct Geo8 {
+  static constexpr int RB = D;                // bytes per row
+  static constexpr int CPR = D / 16;          // 16-byte chunks per row
+  static constexpr int TILE = kBN8 * RB;      // bytes per K or V tile
+  static constexpr int NI = TILE / 1024;      // 1 KB direct loads per tile
+  static constexpr int RPI = 1024 / RB;       // rows per direct load
+  static constexpr int KC = D / 64;           // 64-deep steps of the score contraction
+  static constexpr int NB = D / 32;           // 32-dim output blocks
+  // K: 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank groups.
+  __device__ static int swz_k(int row) { return D == 128 ? (row >> 1) & 7 : (row >> 2) & 3; }
+  // V: the 8 keys x 32 bytes of one half-wave transposing read hit 16 distinct bank groups.
+  __device__ static int swz_v(int row) {
+    return D == 128 ? 2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1) : 2 * ((row >> 3) & 1);
+  }
+};
+
+struct Params8 {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  bf16* o;
+  float* lse;
+  const int32_t* seq_lens;
+  int H, group, Hkv, N, n_qt, total;
+  float sl2;      // scale * q_scale * k_scale * log2(e)
+  float v_scale;  // descale of V
+};
+
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+  // e4m3 for both operands, no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Four e4m3 bytes from four floats (round to nearest even), a first.  The first conversion
+// writes the low half of the word; what it starts from does not matter.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_nondeterministic_value(0), false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void tile_offsets8(int* off, int wave, int lane, bool is_v) {
+  using G = Geo8<D>;
+  constexpr int NI_W = G::NI / NW;
+#pragma unroll
+  for (int t = 0; t < NI_W; ++t) {
+    const int row = (wave * NI_W + t) * G::RPI + lane / G::CPR;
+    const int chunk = (lane % G::CPR) ^ (is_v ? G::swz_v(row) : G::swz_k(row));
+    off[t] = row * G::RB + chunk * 16;
+  }
+}
+
+// Direct global -> LDS copy of one tile (rows key0 .. key0 + 127); rows at or past L read zero.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile8(lds8_t* dst, const uint8_t* head, int key0, int L,
+                                           const int* off, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = Geo8<D>;
+  constexpr int NI_W = G::NI / NW;
+  const int bytes = __builtin_amdgcn_readfirstlane(max(L - key0, 0) * G::RB);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(head + (size_t)key0 * D);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), (short)0, bytes, kBufFlags8);
+#pragma unroll
+  for (int t = 0; t < NI_W; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * NI_W + t) * 1024, 16, off[t],
+                                             0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void wait_loads8() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_fp8_kernel(Params8 p) {
+  using G = Geo8<D>;
+  constexpr int kBM = NW * kWQ8;
+  constexpr int kThreads = 64 * NW;
+  constexpr int NI_W = G::NI / NW;
+  __shared__ __attribute__((aligned(1024))) char k0s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[G::TILE];
+  lds8_t* const K0 = (lds8_t*)k0s;
+  lds8_t* const K1 = (lds8_t*)k1s;
+  lds8_t* const V0 = (lds8_t*)v0s;
+  lds8_t* const V1 = (lds8_t*)v1s;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, hh = lane >> 5;
+
+  // Work unit = (batch, kv head), remapped so its tiles share an XCD (as in the bf16 forward).
+  const int lam = xcd_remap(blockIdx.x, p.total);
+  const int per_unit = p.group * p.n_qt;
+  const int units = p.total / per_unit;
+  int unit = lam / per_unit;
+  const int rem = lam - unit * per_unit;
+  if (units % kXcds8 == 0) unit = (unit % (units / kXcds8)) * kXcds8 + unit / (units / kXcds8);
+  const int b = unit / p.Hkv, g = unit - b * p.Hkv;
+  const int hi = rem / p.n_qt;
+  int qt = rem - hi * p.n_qt;
+  if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
+  const int N = p.N;
+  const int h = g * p.group + hi;
+  const int bh = b * p.H + h;
+  const int L = p.seq_lens != nullptr ? min(max(p.seq_lens[b], 0), N) : N;
+
+  const int q0 = qt * kBM;
+  const uint8_t* Qg = p.q + (size_t)bh * N * D;
+  const uint8_t* Kg = p.k + (size_t)(b * p.Hkv + g) * N * D;
+  const uint8_t* Vg = p.v + (size_t)(b * p.Hkv + g) * N * D;
+  bf16* Og = p.o + (size_t)bh * N * D;
+  float* LSEg = p.lse + (size_t)bh * N;
+
+  if (q0 >= L) {  // padding rows only: O = 0, LSE = -inf
+    const int rows = min(kBM, N - q0);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < rows * (D / 8); i += kThreads)
+      *reinterpret_cast<u32x4*>(Og + (size_t)q0 * D + i * 8) = zero;
+    for (int r = tid; r < rows; r += kThreads) LSEg[q0 + r] = kNegInf;
+    return;
+  }
+
+  const int kv_end = CAUSAL ? min(L, q0 + kBM) : L;
+  const int n_kt = (kv_end + kBN8 - 1) / kBN8;
+  const int qw0 = q0 + wave * kWQ8;
+  const int qrow = qw0 + c32;
+  const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ8) + kBN8 - 1) / kBN8) : n_kt;
+  const float sl2 = p.sl2;
+  int koff[NI_W], voff[NI_W];
+  tile_offsets8<D, NW>(koff, wave, lane, false);
+  tile_offsets8<D, NW>(voff, wave, lane, true);
+  load_tile8<D, NW>(K0, Kg, 0, L, koff, wave);
+  load_tile8<D, NW>(V0, Vg, 0, L, voff, wave);
+
+  // Q fragments (B operand): 32 bytes per 64-deep step, zero for padding rows.
+  i32x8 qf[G::KC];
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c) {
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
+    if (qrow < L) {
+      const uint8_t* src = Qg + (size_t)qrow * D + 64 * c + 32 * hh;
+      lo = *reinterpret_cast<const u32x4*>(src);
+      hi4 = *reinterpret_cast<const u32x4*>(src + 16);
+    }
+    qf[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                  (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+  }
+  // LDS byte offsets: K row reads (row c32 of a 32-key block, chunks 4c + 2h and 4c + 2h + 1)
+  // and the V transposing reads (output block n; keys of read q and key chunk kc are added as
+  // immediate row offsets, which leave the swizzle unchanged).
+  int kaddr[G::KC][2];
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      kaddr[c][e] = c32 * G::RB + (((4 * c + 2 * hh + e) ^ G::swz_k(c32)) << 4);
+  int vaddr[G::NB];
+  {
+    const int grp = lane >> 4, s = lane & 15;
+    const int bb = s >> 1, odd = s & 1, hv = grp >> 1;
+    const int key = 8 * (bb >> 2) + 4 * hv + (bb & 3);
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+      const int dim = 32 * n + 16 * (grp & 1) + 8 * odd;
+      vaddr[n] = key * G::RB + (((dim >> 4) ^ G::swz_v(key)) << 4) + (dim & 15);
+    }
+  }
+
+  f32x16 acc[G::NB];
+#pragma unroll
+  for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
+  float m_run = kNegInf;  // running maximum (log2 units)
+  float l_run = 0.f;      // this lane's share of the row sum, times 256
+
+  auto tile = [&](const lds8_t* Kc, const lds8_t* Vc, int key0, auto masked) __attribute__((always_inline)) {
+    constexpr bool M = decltype(masked)::value;
+    constexpr int NS = 2 * G::KC;  // score MFMAs of a 64-key block
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      f32x16 s[2];
+      // Scores of keys 64 hk .. 64 hk + 63: two 16-byte K reads per MFMA, kAhead8 MFMAs ahead.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bl = 0; bl < 2; ++bl) {
+        s[bl] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < G::KC; ++c) {
+          const lds8_t* rb = Kc + (64 * hk + 32 * bl) * G::RB;
+          const u32x4 a0 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][0]);
+          const u32x4 a1 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][1]);
+          const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          s[bl] = mfma8(af, qf[c], s[bl]);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2 * kAhead8, 0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma8, 1, 0);
+        if (i + kAhead8 < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (M) {
+        // Element r of block bl is key key0 + 4 hh + c with the constant c below; it is masked
+        // when c exceeds one per-lane threshold (past the length, or after the query row).
+        const int base = key0 + 4 * hh;
+        const int thr = CAUSAL ? min(L - 1, qrow) - base : L - 1 - base;
+#pragma unroll
+        for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 64 * hk + 32 * bl + 8 * (r >> 2) + (r & 3);
+            if (c > thr) s[bl][r] = kNegInf;
+          }
+      }
+      // Online softmax over this block: running maximum, rescale only when it grew.
+      float mx = s[0][0];
+#pragma unroll
+      for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bl][r]);
+      mx = max_xor32(mx);
+      const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {  // some row's maximum grew
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - m_new);  // 0 before any visible key
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
+      }
+      const float bias = (m_run == kNegInf ? 0.f : m_run) - (float)kPScaleLog2;  // p times 256
+      // Probabilities as e4m3 in k-slot order (the B operand of P V), their unrounded sum.
+      i32x8 pf;
+      float rs = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float x = s[w >> 2][4 * (w & 3) + t];
+          float arg = fmaf(x, sl2, -bias);
+          if (M && x == kNegInf) arg = kNegInf;  // exactly 0, also when the scale is 0
+          e[t] = fast_exp2(arg);
+        }
+        rs += (e[0] + e[1]) + (e[2] + e[3]);
+        pf[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+      }
+      l_run += rs;
+      // P V: per output block four transposing V reads (keys 64 hk + 16 q ..) and one MFMA.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) {
+        i32x8 vf;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)(Vc + vaddr[n] + (64 * hk + 16 * q) * G::RB));
+          vf[2 * q] = r2[0];
+          vf[2 * q + 1] = r2[1];
+        }
+        acc[n] = mfma8(vf, pf, acc[n]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4 * kAheadV8, 0);
+#pragma unroll
+      for (int i = 0; i < G::NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma8, 1, 0);
+        if (i + kAheadV8 < G::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // The LDS loads that follow (the next block's K fragments) may be given the registers
+      // that still hold P and V^T for the last of these MFMAs.  The compiler inserts no wait
+      // between an MFMA and a later LDS load into its source registers, and with the 64-deep
+      // FP8 MFMA such a load can land before the operands are consumed (measured: corrupted
+      // output accumulators, gone with a wait here).  Wait out one MFMA (16 passes) first.
+      asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int n_main = CAUSAL ? min(q0, L) / kBN8 : L / kBN8;
+  auto iter = [&](int j, auto parity, auto masked) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(parity)::value;
+    lds8_t* const Kc = ODD ? K1 : K0;
+    lds8_t* const Vc = ODD ? V1 : V0;
+    lds8_t* const Kn = ODD ? K0 : K1;
+    lds8_t* const Vn = ODD ? V0 : V1;
+    if (j + 1 < n_kt) {
+      load_tile8<D, NW>(Kn, Kg, (j + 1) * kBN8, L, koff, wave);
+      load_tile8<D, NW>(Vn, Vg, (j + 1) * kBN8, L, voff, wave);
+    }
+    if (j < n_kw) tile(Kc, Vc, j * kBN8, masked);
+    wait_loads8();
+    __syncthreads();
+  };
+  wait_loads8();
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < n_main; j += 2) {
+    iter(j, std::false_type{}, std::false_type{});
+    iter(j + 1, std::true_type{}, std::false_type{});
+  }
+  for (; j < n_kt; ++j) {
+    if (j & 1) iter(j, std::true_type{}, std::true_type{});
+    else iter(j, std::false_type{}, std::true_type{});
+  }
+
+  // Epilogue: O = v_scale * acc / l (both carry the factor 256); LSE = ln 2 (m + log2 l - 8).
+  const float lt = add_xor32(l_run);
+  if (qrow < N) {
+    const bool valid = qrow < L;
+    const float f = valid ? p.v_scale / lt : 0.f;
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[n][4 * r4 + 0] * f, acc[n][4 * r4 + 1] * f);
+        w[1] = pack_bf16x2(acc[n][4 * r4 + 2] * f, acc[n][4 * r4 + 3] * f);
+        *reinterpret_cast<u32x2*>(Og + (size_t)qrow * D + n * 32 + 8 * r4 + 4 * hh) = w;
+      }
+    }
+    if (hh == 0) LSEg[qrow] = valid ? (m_run + __log2f(lt) - (float)kPScaleLog2) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
+  Params8 p;
+  p.q = static_cast<const uint8_t*>(a.q);
+  p.k = static_cast<const uint8_t*>(a.k);
+  p.v = static_cast<const uint8_t*>(a.v);
+  p.o = static_cast<bf16*>(a.o);
+  p.lse = a.lse;
+  p.seq_lens = a.seq_lens;
+  p.H = a.H;
+  p.group = a.H / a.Hkv;
+  p.Hkv = a.Hkv;
+  p.N = a.N;
+  p.sl2 = a.scale * a.q_scale * a.k_scale * kLog2e;
+  p.v_scale = a.v_scale;
+  const long long wide = (long long)a.B * a.H * ((a.N + 8 * kWQ8 - 1) / (8 * kWQ8));
+  if (wide >= kCUs8) {
+    p.n_qt = (a.N + 8 * kWQ8 - 1) / (8 * kWQ8);
+    p.total = a.B * a.H * p.n_qt;
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 8>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+  } else {
+    p.n_qt = (a.N + 4 * kWQ8 - 1) / (4 * kWQ8);
+    p.total = a.B * a.H * p.n_qt;
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 4>), dim3(p.total), dim3(64 * 4), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return a.causal ? launch8<128, true>(a, stream) : launch8<128, false>(a, stream);
+  return a.causal ? launch8<64, true>(a, stream) : launch8<64, false>(a, stream);
+}
+
+}  // namespace fa

@@ -21,6 +21,21 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+
+struct Fp8FwdArgs {
+  const void* q;  // e4m3 codes
+  const void* k;
+  const void* v;
+  float q_scale, k_scale, v_scale;  // per-tensor descale factors
+  void* o;                          // bf16
+  float* lse;
+  const int32_t* seq_lens;
+  int B, H, Hkv, N, d;
+  float scale;
+  bool causal;
+};
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 struct DecodeArgs {

@@ -32,6 +32,7 @@ __all__ = [
     "varlen_lengths",
     "paged_decode_inputs",
     "WORKLOADS",
+    "fp8_inputs",
 ]
 
 # The five workloads the measurements and parity cases are quoted on.
@@ -44,6 +45,10 @@ WORKLOADS = {
                           len_lo=2048, len_hi=8192),
     "paged_decode": dict(S=64, Hq=32, Hkv=8, d=128, block_size=16, len_lo=512, len_hi=32768,
                          seed=5),
+    # FP8 forward: the 16K prefill shapes with e4m3 inputs (per-tensor scales)
+    "fp8_16k": dict(B=1, H=8, Hkv=8, N=16384, d=128, causal=False, seed=7),
+    "fp8_16k_causal": dict(B=1, H=8, Hkv=8, N=16384, d=128, causal=True, seed=7),
+    "fp8_4k": dict(B=1, H=8, Hkv=8, N=4096, d=128, causal=False, seed=8),
     # chunked prefill against the paged cache: chunks of up to 1024 new tokens
     "paged_prefill": dict(S=16, Hq=32, Hkv=8, d=128, max_q=1024, block_size=16, len_lo=1024,
                           len_hi=32768, seed=6),
@@ -80,6 +85,27 @@ def prefill_inputs(B, H, Hkv, N, d, dtype="bf16", seed=0, len_lo=None, len_hi=No
     if len_lo is not None:
         seq_lens = varlen_lengths(B, len_lo, len_hi, g)
     return q, k, v, seq_lens
+
+
+def fp8_inputs(B, H, Hkv, N, d, seed=0, len_lo=None, len_hi=None):
+    """(q8, k8, v8, (q_scale, k_scale, v_scale), seq_lens) on the CPU.
+
+    The bf16 N(0,1) tensors of ``prefill_inputs`` quantised per tensor the usual way: descale
+    factor amax / 448 (the largest e4m3 value), codes = the tensor divided by it, rounded to
+    e4m3 by torch's float8_e4m3fn cast and returned as uint8.
+    """
+    q, k, v, seq_lens = prefill_inputs(B, H, Hkv, N, d, "bf16", seed, len_lo, len_hi)
+    codes, scales = [], []
+    for t in (q, k, v):
+        sc = float(t.float().abs().max()) / 448.0
+        c = torch.empty(t.shape, dtype=torch.uint8)
+        flat, src = c.view(-1), t.view(-1)
+        for s0 in range(0, src.numel(), 1 << 26):  # bounded host memory
+            s1 = min(src.numel(), s0 + (1 << 26))
+            flat[s0:s1] = (src[s0:s1].float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+        codes.append(c)
+        scales.append(sc)
+    return codes[0], codes[1], codes[2], tuple(scales), seq_lens
 
 
 def output_gradient(B, H, N, d, dtype="bf16", seed=0):

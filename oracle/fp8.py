@@ -18,7 +18,7 @@ asynchronous pipeline on the H100) without fixing the arithmetic.  The reading t
   is the exact log-sum-exp of the scaled scores.
 
 Because the rounding of p happens relative to the running maximum of each block, the result
-depends on the block size; ``block`` must equal the fused kernel's key tile (128).  With
+depends on the block size; ``block`` must equal the fused kernel's softmax block (64 keys).  With
 ``p_scale=None`` nothing is rounded and the function is the exact attention of the dequantised
 inputs (pinned against the three-pass oracle).
 
@@ -72,14 +72,17 @@ def e4m3_round(x):
 
 
 def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False, seq_lens=None,
-                      block=128, p_scale=256.0):
+                      block=64, p_scale=256.0, rows=None):
     """FP8 attention forward: (O [B, H, N, d], LSE [B, H, N]) in float64.
 
     q8 [B, H, N, d], k8 and v8 [B, Hkv, N, d]: e4m3 byte codes (uint8).  q_scale, k_scale,
     v_scale: per-tensor descale factors.  scale: the softmax scale of the scores.  causal,
     seq_lens, grouped-query heads and padding as for ``attention_ref``.  block: keys per block of
     the online softmax.  p_scale: the factor applied before rounding probabilities to e4m3, or
-    None for no rounding.
+    None for no rounding.  rows: None, or a 1-D list of query rows; then only those rows are
+    computed (each row's recurrence involves that row alone) and the results are
+    [B, H, n_rows, d] and [B, H, n_rows] (rows at or past a sequence's length: O = 0,
+    LSE = -inf).
     """
     q = e4m3_decode(q8) * float(q_scale)
     k = e4m3_decode(k8) * float(k_scale)
@@ -87,19 +90,21 @@ def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False
     B, H, Hkv, N, d = _check_shapes(q, k, v)
     group = H // Hkv
     lens = _lengths(seq_lens, B, N)
-    o = np.zeros((B, H, N, d))
-    lse = np.full((B, H, N), -np.inf)
+    sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    o = np.zeros((B, H, sel.size, d))
+    lse = np.full((B, H, sel.size), -np.inf)
     for b in range(B):
         L = lens[b]
-        if L == 0:
+        valid = sel < L
+        if L == 0 or not valid.any():
             continue
-        counts = _visible_keys(np.arange(L), L, causal)
+        counts = _visible_keys(sel[valid], L, causal)
         for h in range(H):
             g = h // group
-            ob, lb = _online(q[b, h, :L], k[b, g, :L], v[b, g, :L], float(scale), counts, block,
-                             p_scale)
-            o[b, h, :L] = ob
-            lse[b, h, :L] = lb
+            ob, lb = _online(q[b, h, sel[valid]], k[b, g, :L], v[b, g, :L], float(scale), counts,
+                             block, p_scale)
+            o[b, h, valid] = ob
+            lse[b, h, valid] = lb
     return o, lse
 
 

@@ -32,7 +32,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_unfused",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_fp8",
+                                     "fa_fwd_unfused",
                                      "fa_fwd_unfused_workspace_bytes", "fa_paged_decode",
                                      "fa_paged_decode_workspace_bytes", "fa_paged_prefill",
                                      "fa_status_str"]
@@ -80,6 +81,31 @@ def _fwd(lib, **kw):
 ])
 def test_fwd_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
+
+
+def _fp8(lib, **kw):
+    a = dict(q=P, k=P, v=P, qs=0.01, ks=0.01, vs=0.01, o=P, lse=P, B=1, H=8, Hkv=2, N=128, d=128,
+             scale=0.1, causal=0, seq_lens=None, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"],
+                          a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"],
+                          a["seq_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(Hkv=0), INVALID), (dict(N=0), INVALID),
+    (dict(d=0), INVALID), (dict(H=8, Hkv=3), INVALID),
+    (dict(k=P + 8), INVALID), (dict(o=P + 4), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(seq_lens=P + 1), INVALID),
+    (dict(scale=-0.5), INVALID), (dict(qs=math.nan), INVALID), (dict(ks=-1.0), INVALID),
+    (dict(vs=math.inf), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 20), UNSUPPORTED),
+])
+def test_fp8_rejects(lib, kw, status):
+    assert _fp8(lib, **kw) == status
 
 
 def test_bwd_workspace_bytes(lib):
@@ -193,6 +219,7 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     assert _bwd(lib) == HIPERR
     assert _pre(lib) == HIPERR
     assert _unf(lib) == HIPERR
+    assert _fp8(lib) == HIPERR
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

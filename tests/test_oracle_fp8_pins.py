@@ -163,3 +163,15 @@ def test_rounding_error_within_e4m3_bound():
         err = np.abs(o[0, h] - ro[0, h])
         assert (err <= bound).all()
         assert err.max() > 0
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, [9, 300])])
+def test_row_subset_equals_full(causal, lens):
+    rng = np.random.default_rng(37)
+    q8, k8, v8 = _random_case(rng, 2, 2, 1, 300, 8)
+    full = attention_fp8_ref(q8, k8, v8, 0.01, 0.01, 0.01, 0.3, causal=causal, seq_lens=lens)
+    rows = [299, 0, 150, 8, 9]
+    sub = attention_fp8_ref(q8, k8, v8, 0.01, 0.01, 0.01, 0.3, causal=causal, seq_lens=lens,
+                            rows=rows)
+    np.testing.assert_allclose(sub[0], full[0][:, :, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sub[1], full[1][:, :, rows], rtol=0, atol=1e-13)
