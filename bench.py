@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,bwd,prefill_paged,decode,copy} [--steps K]   (one op)
+    python bench.py --only {fwd,fwd_causal,fwd_fp8,bwd,prefill_paged,decode,copy} [--steps K]
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -51,8 +51,11 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def _time_calls(torch, fn, iters):
-    """Average ms of fn() over iters calls, HIP events on the current stream."""
+def _time_calls(torch, fn, iters, warmup=3):
+    """Average ms of fn() over iters calls after `warmup` untimed ones, HIP events on the
+    current stream."""
+    for _ in range(warmup):
+        fn()
     evs = [_events(torch) for _ in range(iters)]
     for a, b in evs:
         a.record()
@@ -115,6 +118,16 @@ def only(args, torch, dev, wf, wd):
         causal = args.only == "fwd_causal"
         fn = lambda: fa_fwd(q, k, v, o, lse, causal=causal)  # noqa: E731
         what = f"fa_fwd B=1 H=8 N=16384 d=128 bf16 causal={causal}"
+    elif args.only == "fwd_fp8":
+        from io_aware_attention_02_amd import fa_fwd_fp8
+        from io_aware_attention_02_amd.inputs import WORKLOADS, fp8_inputs
+        w8 = WORKLOADS["fp8_16k"]
+        q8, k8, v8, sc8, _ = fp8_inputs(w8["B"], w8["H"], w8["Hkv"], w8["N"], w8["d"], seed=w8["seed"])
+        q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+        o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+        fn = lambda: fa_fwd_fp8(q8, k8, v8, *sc8, o=o8, lse=l8)  # noqa: E731
+        what = "fa_fwd_fp8 B=1 H=8 N=16384 d=128 e4m3 non-causal"
     elif args.only == "bwd":
         from io_aware_attention_02_amd import fa_bwd
         from io_aware_attention_02_amd.inputs import output_gradient
@@ -152,7 +165,7 @@ def only(args, torch, dev, wf, wd):
     for _ in range(args.warmup):
         fn()
     torch.cuda.synchronize()
-    ms = _time_calls(torch, fn, args.steps)
+    ms = _time_calls(torch, fn, args.steps, warmup=0)
     print(json.dumps({"only": args.only, "what": what, "calls": args.steps, "ms_per_call": round(ms, 4)}),
           flush=True)
 
@@ -164,7 +177,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_causal", "bwd", "prefill_paged", "decode", "copy"],
+    ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_fp8", "bwd", "prefill_paged",
+                                       "decode", "copy"],
                     default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
@@ -350,6 +364,21 @@ def main():
                                                   workspace=wsb), 10)
             f = acc.attention_bwd_flops(wf["B"], wf["H"], wf["N"], wf["d"], causal=causal)
             extras[name] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2)}
+        # FP8 forward (e4m3 Q, K, V with per-tensor scales) on the 16K shapes, both masks.
+        from io_aware_attention_02_amd import fa_fwd_fp8
+        from io_aware_attention_02_amd.inputs import fp8_inputs
+        w8 = WORKLOADS["fp8_16k"]
+        q8, k8, v8, sc8, _ = fp8_inputs(w8["B"], w8["H"], w8["Hkv"], w8["N"], w8["d"], seed=w8["seed"])
+        q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+        o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+        for causal, name in ((False, "fp8_16k"), (True, "fp8_16k_causal")):
+            t = _time_calls(torch, lambda: fa_fwd_fp8(q8, k8, v8, *sc8, o=o8, lse=l8, causal=causal), 20,
+                            warmup=20)
+            f = acc.attention_flops(w8["B"], w8["H"], w8["N"], w8["d"], causal=causal)
+            extras[name] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
+                            "frac_of_fp8_peak": round(f / t / 1e9 / acc.MI355X_FP8_DENSE_TFLOPS, 4)}
+        del q8, k8, v8
         out["extras"] = extras
 
     if not args.no_cpu_baseline:

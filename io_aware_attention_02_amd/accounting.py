@@ -30,10 +30,12 @@ __all__ = [
     "qkv_bytes",
     "kv_cache_bytes",
     "MI355X_BF16_DENSE_TFLOPS",
+    "MI355X_FP8_DENSE_TFLOPS",
     "MI355X_HBM_GBPS",
 ]
 
 MI355X_BF16_DENSE_TFLOPS = 2500.0   # published dense bf16 matrix peak
+MI355X_FP8_DENSE_TFLOPS = 5000.0    # published dense fp8 matrix peak
 MI355X_HBM_GBPS = 8000.0            # published HBM3E peak
 
 
