@@ -104,6 +104,33 @@ __device__ __forceinline__ void load_tile_paged(lds_t* dst, const bf16* cache, i
 #endif
 }
 
+// Paged chunked prefill: the sequence a workgroup serves, taken in order of decreasing work
+// (context length times chunk length, ties by index), so that the longest sequences start first
+// and the short ones fill in behind them.  Every workgroup ranks the sequences itself, one
+// thread per sequence against lengths staged in LDS; with more than kMaxRanked sequences the
+// natural order is kept.  The order changes no result.
+constexpr int kMaxRanked = 512;
+template <int NW>
+__device__ int by_work(const Params& p, int pos, int* buf) {
+  const int S = p.total / (p.H * p.n_qt);
+  if (S > kMaxRanked) return pos;
+  int* w = buf;                   // work of each sequence, saturated to 31 bits
+  int* order = buf + kMaxRanked;  // sequence at each rank
+  for (int i = threadIdx.x; i < S; i += 64 * NW) {
+    const int L = min(max(p.seq_lens[i], 0), p.max_blocks * kPageRows);
+    const int Q = min(max(p.q_lens[i], 0), min(L, p.N));
+    w[i] = (int)min((long long)L * Q, (long long)0x7fffffff);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < S; i += 64 * NW) {
+    int r = 0;
+    for (int t = 0; t < S; ++t) r += (w[t] > w[i]) || (w[t] == w[i] && t < i);
+    order[r] = i;
+  }
+  __syncthreads();
+  return order[pos];
+}
+
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   float m0 = s[0][0], m1 = s[1][0];
 #pragma unroll
@@ -193,6 +220,7 @@ fwd_bf16_kernel(Params p) {
   lds_t* const K1 = (lds_t*)k1s;
   lds_t* const V0 = (lds_t*)v0s;
   lds_t* const V1 = (lds_t*)v1s;
+  __shared__ int rank_buf[PAGED ? 2 * kMaxRanked : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -208,7 +236,9 @@ fwd_bf16_kernel(Params p) {
   int unit = lam / per_unit;
   const int rem = lam - unit * per_unit;
   if (units % kXcds == 0) unit = (unit % (units / kXcds)) * kXcds + unit / (units / kXcds);
-  const int b = unit / p.Hkv, g = unit - b * p.Hkv;
+  int b = unit / p.Hkv;
+  const int g = unit - b * p.Hkv;
+  if constexpr (PAGED) b = by_work<NW>(p, b, rank_buf);  // heaviest sequences first
   const int hi = rem / p.n_qt;
   int qt = rem - hi * p.n_qt;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
@@ -243,8 +273,10 @@ fwd_bf16_kernel(Params p) {
   const int n_kt = (kv_end + kBN - 1) / kBN;
   const int qw0 = q0 + wave * kWQ;
   const int qrow = qw0 + c32;
-  // Tiles this wave needs (fewer than n_kt on the causal diagonal).
-  const int n_kw = CAUSAL ? min(n_kt, (min(L, off + qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
+  // Tiles this wave needs (fewer than n_kt on the causal diagonal; none for a paged chunk's
+  // wave whose rows are all padding, common when chunks are much shorter than the query tile).
+  const int n_kw = (PAGED && qw0 >= Lq) ? 0
+                 : CAUSAL ? min(n_kt, (min(L, off + qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
   const float sl2 = p.sl2;
   int koff[NI_W], voff[NI_W];
   if constexpr (PAGED) {
@@ -471,16 +503,11 @@ hipError_t launch_paged(const PagedPrefillArgs& a, hipStream_t stream) {
   p.N = a.max_q;
   p.max_blocks = a.max_blocks;
   p.sl2 = a.scale * kLog2e;
-  const long long wide = (long long)a.S * a.Hq * ((a.max_q + 8 * kWQ - 1) / (8 * kWQ));
-  if (wide >= kCUs) {
-    p.n_qt = (a.max_q + 8 * kWQ - 1) / (8 * kWQ);
-    p.total = a.S * a.Hq * p.n_qt;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 8, true>), dim3(p.total), dim3(64 * 8), 0, stream, p);
-  } else {
-    p.n_qt = (a.max_q + 4 * kWQ - 1) / (4 * kWQ);
-    p.total = a.S * a.Hq * p.n_qt;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4, true>), dim3(p.total), dim3(64 * 4), 0, stream, p);
-  }
+  // Four waves (128 query rows) per workgroup, two workgroups per CU: chunks are often much
+  // shorter than 256 rows, and a wave whose rows are all padding idles its SIMD.
+  p.n_qt = (a.max_q + 4 * kWQ - 1) / (4 * kWQ);
+  p.total = a.S * a.Hq * p.n_qt;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4, true>), dim3(p.total), dim3(64 * 4), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -186,7 +186,8 @@ fwd_fp8_kernel(Params8 p) {
   const int n_kt = (kv_end + kBN8 - 1) / kBN8;
   const int qw0 = q0 + wave * kWQ8;
   const int qrow = qw0 + c32;
-  const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ8) + kBN8 - 1) / kBN8) : n_kt;
+  const int n_kw = qw0 >= L ? 0  // every row of this wave is padding
+                 : CAUSAL ? min(n_kt, (min(L, qw0 + kWQ8) + kBN8 - 1) / kBN8) : n_kt;
   const float sl2 = p.sl2;
   int koff[NI_W], voff[NI_W];
   tile_offsets8<D, NW>(koff, wave, lane, false);

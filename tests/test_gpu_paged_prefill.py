@@ -2,8 +2,8 @@
 
 Each sequence's newest Q_b tokens attend, causally with the offset L_b - Q_b, to every cached
 token gathered through the block table.  Shapes cover chunk lengths 0, 1, a few, a full tile
-and the whole sequence, short and long caches, d = 64 and 128, grouped-query heads, and both
-workgroup sizes the launch picks (4 and 8 waves).
+and the whole sequence, short and long caches, d = 64 and 128, grouped-query heads, and
+sequences of very different work (the kernel serves them heaviest first).
 """
 
 import numpy as np
