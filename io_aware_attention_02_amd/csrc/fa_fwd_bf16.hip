@@ -104,21 +104,26 @@ __device__ __forceinline__ void load_tile_paged(lds_t* dst, const bf16* cache, i
 #endif
 }
 
-// Paged chunked prefill: the sequence a workgroup serves, taken in order of decreasing work
-// (context length times chunk length, ties by index), so that the longest sequences start first
-// and the short ones fill in behind them.  Every workgroup ranks the sequences itself, one
-// thread per sequence against lengths staged in LDS; with more than kMaxRanked sequences the
-// natural order is kept.  The order changes no result.
+// With per-sequence lengths (varlen prefill, paged chunked prefill): the sequence a workgroup
+// serves, taken in order of decreasing work (key length times query rows, ties by index), so
+// that the longest sequences start first and the short ones fill in behind them.  Every
+// workgroup ranks the sequences itself, one thread per sequence against lengths staged in LDS;
+// with more than kMaxRanked sequences the natural order is kept.  The order changes no result.
 constexpr int kMaxRanked = 512;
-template <int NW>
+template <int NW, bool PAGED>
 __device__ int by_work(const Params& p, int pos, int* buf) {
   const int S = p.total / (p.H * p.n_qt);
   if (S > kMaxRanked) return pos;
   int* w = buf;                   // work of each sequence, saturated to 31 bits
   int* order = buf + kMaxRanked;  // sequence at each rank
   for (int i = threadIdx.x; i < S; i += 64 * NW) {
-    const int L = min(max(p.seq_lens[i], 0), p.max_blocks * kPageRows);
-    const int Q = min(max(p.q_lens[i], 0), min(L, p.N));
+    int L, Q;
+    if constexpr (PAGED) {
+      L = min(max(p.seq_lens[i], 0), p.max_blocks * kPageRows);
+      Q = min(max(p.q_lens[i], 0), min(L, p.N));
+    } else {
+      L = Q = min(max(p.seq_lens[i], 0), p.N);
+    }
     w[i] = (int)min((long long)L * Q, (long long)0x7fffffff);
   }
   __syncthreads();
@@ -220,7 +225,7 @@ fwd_bf16_kernel(Params p) {
   lds_t* const K1 = (lds_t*)k1s;
   lds_t* const V0 = (lds_t*)v0s;
   lds_t* const V1 = (lds_t*)v1s;
-  __shared__ int rank_buf[PAGED ? 2 * kMaxRanked : 1];
+  __shared__ int rank_buf[2 * kMaxRanked];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -238,7 +243,7 @@ fwd_bf16_kernel(Params p) {
   if (units % kXcds == 0) unit = (unit % (units / kXcds)) * kXcds + unit / (units / kXcds);
   int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
-  if constexpr (PAGED) b = by_work<NW>(p, b, rank_buf);  // heaviest sequences first
+  if (PAGED || p.seq_lens != nullptr) b = by_work<NW, PAGED>(p, b, rank_buf);  // heaviest first
   const int hi = rem / p.n_qt;
   int qt = rem - hi * p.n_qt;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
