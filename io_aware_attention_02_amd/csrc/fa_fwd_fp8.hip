@@ -6,11 +6,12 @@
 // v_mfma_f32_32x32x64_f8f6f4 (64-deep contraction, fp32 accumulation): the scores S^T = K Q^T
 // from the codes (the descale factors fold into the softmax scale), and O^T += V^T P^T with the
 // probabilities rounded to e4m3.  The softmax is the online recurrence of "FlashAttention优化"
-// §3.2.1 over blocks of 64 keys: the probabilities of a block are relative to the running
-// maximum, exp(s - m) <= 1, and are multiplied by 256 before the rounding so that small values
-// stay out of the e4m3 subnormals; the row sum uses them unrounded, and the output is
-// multiplied by v_scale / sum at the end.  The output and sum are rescaled only when some row's
-// maximum grew (after the first blocks, rarely).
+// §3.2.1 over blocks of 64 keys with a per-row reference m that moves to a block's maximum only
+// when that maximum exceeds it by more than a factor 2^2: the probabilities exp(s - m) <= 4 are
+// multiplied by 64 before the rounding (at most 256, inside the e4m3 range, and small values
+// stay out of the subnormals); the row sum uses them unrounded, and the output is multiplied
+// by v_scale / sum at the end.  Output and sum are rescaled only when some row's reference
+// moves, which after the first blocks is rare.
 //
 // CDNA4 mapping:
 //  * A wave owns 32 query rows, an LDS tile is 128 keys (two softmax blocks); workgroups of 8
@@ -48,7 +49,8 @@ constexpr int kCUs8 = 256;
 constexpr int kXcds8 = 8;
 constexpr int kWQ8 = 32;               // query rows per wave
 constexpr int kBN8 = 128;              // keys per tile
-constexpr int kPScaleLog2 = 8;         // probabilities are rounded to e4m3 as 256 p
+constexpr int kPScaleLog2 = 6;         // probabilities are rounded to e4m3 as 64 p
+constexpr float kLagLog2 = 2.f;        // a row's reference moves when outgrown by more than 2^2
 constexpr int kBufFlags8 = 0x00020000; // buffer resource word 3: 32-bit data format, raw
 constexpr int kSchedMfma8 = 0x008;     // instruction-group masks of sched_group_barrier
 constexpr int kSchedDsRead8 = 0x100;
@@ -90,9 +92,10 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // Four e4m3 bytes from four floats (round to nearest even), a first.  The first conversion
-// writes the low half of the word; what it starts from does not matter.
+// writes the low half of the word and keeps the high half of its third operand, which the
+// second overwrites; a's own bits serve, so the conversion can reuse a's register in place.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_nondeterministic_value(0), false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -232,8 +235,8 @@ fwd_fp8_kernel(Params8 p) {
   f32x16 acc[G::NB];
 #pragma unroll
   for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
-  float m_run = kNegInf;  // running maximum (log2 units)
-  float l_run = 0.f;      // this lane's share of the row sum, times 256
+  float m_run = kNegInf;  // row reference (log2 units): a maximum, at most 2 below the current one
+  float l_run = 0.f;      // this lane's share of the row sum, times 64
 
   auto tile = [&](const lds8_t* Kc, const lds8_t* Vc, int key0, auto masked) __attribute__((always_inline)) {
     constexpr bool M = decltype(masked)::value;
@@ -276,7 +279,8 @@ fwd_fp8_kernel(Params8 p) {
             if (c > thr) s[bl][r] = kNegInf;
           }
       }
-      // Online softmax over this block: running maximum, rescale only when it grew.
+      // Online softmax over this block: the reference moves (and output and sum are rescaled)
+      // only for rows whose maximum outgrew it by more than 2^kLagLog2.
       float mx = s[0][0];
 #pragma unroll
       for (int bl = 0; bl < 2; ++bl)
@@ -284,15 +288,16 @@ fwd_fp8_kernel(Params8 p) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bl][r]);
       mx = max_xor32(mx);
       const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {  // some row's maximum grew
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2(m_run - m_new);  // 0 before any visible key
+      const bool grow = mt > m_run + kLagLog2;  // -inf + 2 = -inf: the first key always moves it
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 before any visible key
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
       }
-      const float bias = (m_run == kNegInf ? 0.f : m_run) - (float)kPScaleLog2;  // p times 256
+      const float bias = (m_run == kNegInf ? 0.f : m_run) - (float)kPScaleLog2;  // p times 64
       // Probabilities as e4m3 in k-slot order (the B operand of P V), their unrounded sum.
       i32x8 pf;
       float rs = 0.f;
@@ -368,7 +373,7 @@ fwd_fp8_kernel(Params8 p) {
     else iter(j, std::false_type{}, std::true_type{});
   }
 
-  // Epilogue: O = v_scale * acc / l (both carry the factor 256); LSE = ln 2 (m + log2 l - 8).
+  // Epilogue: O = v_scale * acc / l (both carry the factor 64); LSE = ln 2 (m + log2 l - 6).
   const float lt = add_xor32(l_run);
   if (qrow < N) {
     const bool valid = qrow < L;

@@ -10,12 +10,14 @@ asynchronous pipeline on the H100) without fixing the arithmetic.  The reading t
   code c of Q is ``q_scale * e4m3(c)`` (likewise K, V).
 * The attention computed is the one of the dequantised tensors, O = softmax(scale * Q K^T) V,
   with the online softmax of "FlashAttention优化" (coreui.cn) §3.2.1: the keys are visited in
-  blocks of ``block`` keys, a running row maximum m and sum l are kept, and the accumulated
-  output and sum are rescaled by exp(m_old - m_new) whenever the maximum grows.
-* The probabilities of a block, p = exp(s - m_new) in (0, 1], enter the P V product as FP8:
-  ``e4m3_round(p_scale * p) / p_scale`` (p_scale = 256 spends the e4m3 range above 1 on keeping
-  small probabilities out of the subnormals).  The row sum l uses the unrounded p, so the LSE
-  is the exact log-sum-exp of the scaled scores.
+  blocks of ``block`` keys, a per-row reference m and sum l are kept, and the accumulated
+  output and sum are rescaled by exp(m_old - m_new) whenever the reference moves.  The
+  reference moves to a block's maximum only when that maximum exceeds it by more than
+  ``lag`` (in log2 units, i.e. a factor 2^lag); lag = 0 is the plain running maximum.
+* The probabilities of a block, p = exp(s - m) in (0, 2^lag], enter the P V product as FP8:
+  ``e4m3_round(p_scale * p) / p_scale`` (p_scale = 64 with lag = 2 keeps 64 p <= 256 inside
+  the e4m3 range and small probabilities out of the subnormals).  The row sum l uses the
+  unrounded p, so the LSE is the exact log-sum-exp of the scaled scores.
 
 Because the rounding of p happens relative to the running maximum of each block, the result
 depends on the block size; ``block`` must equal the fused kernel's softmax block (64 keys).  With
@@ -72,14 +74,15 @@ def e4m3_round(x):
 
 
 def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False, seq_lens=None,
-                      block=64, p_scale=256.0, rows=None):
+                      block=64, p_scale=64.0, lag=2.0, rows=None):
     """FP8 attention forward: (O [B, H, N, d], LSE [B, H, N]) in float64.
 
     q8 [B, H, N, d], k8 and v8 [B, Hkv, N, d]: e4m3 byte codes (uint8).  q_scale, k_scale,
     v_scale: per-tensor descale factors.  scale: the softmax scale of the scores.  causal,
     seq_lens, grouped-query heads and padding as for ``attention_ref``.  block: keys per block of
     the online softmax.  p_scale: the factor applied before rounding probabilities to e4m3, or
-    None for no rounding.  rows: None, or a 1-D list of query rows; then only those rows are
+    None for no rounding.  lag: how far (log2 units) a block's maximum may exceed the row's
+    reference before the reference moves.  rows: None, or a 1-D list of query rows; then only those rows are
     computed (each row's recurrence involves that row alone) and the results are
     [B, H, n_rows, d] and [B, H, n_rows] (rows at or past a sequence's length: O = 0,
     LSE = -inf).
@@ -102,14 +105,15 @@ def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False
         for h in range(H):
             g = h // group
             ob, lb = _online(q[b, h, sel[valid]], k[b, g, :L], v[b, g, :L], float(scale), counts,
-                             block, p_scale)
+                             block, p_scale, float(lag) * np.log(2.0))
             o[b, h, valid] = ob
             lse[b, h, valid] = lb
     return o, lse
 
 
-def _online(qb, kb, vb, scale, counts, block, p_scale):
-    """Online softmax over key blocks for the rows of one sequence (every row sees >= 1 key)."""
+def _online(qb, kb, vb, scale, counts, block, p_scale, lag):
+    """Online softmax over key blocks for the rows of one sequence (every row sees >= 1 key).
+    lag is in natural-log units here."""
     n, L = qb.shape[0], kb.shape[0]
     s = scale * (qb @ kb.T)
     s = np.where(np.arange(L)[None, :] >= counts[:, None], -np.inf, s)
@@ -119,7 +123,7 @@ def _online(qb, kb, vb, scale, counts, block, p_scale):
     for j0 in range(0, L, block):
         sj = s[:, j0:j0 + block]
         bm = sj.max(axis=1)
-        m_new = np.maximum(m, bm)
+        m_new = np.where(bm > m + lag, bm, m)   # m = -inf: the first visible key sets it
         # rows with no visible key so far keep m = -inf and add nothing
         seen = m_new > -np.inf
         ref = np.where(seen, m_new, 0.0)

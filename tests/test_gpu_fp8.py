@@ -14,7 +14,7 @@ comparisons:
   row's largest probability exp(max_j S_ij - LSE_i) and FLIPS = 2 flipped keys per row.
 * against the exact attention of the dequantised inputs (small shapes): every rounded
   probability is within one e4m3 step of the exact one, so |O - O_exact| <= 2^-3 sum_j P_ij |V_j|
-  + 2^-18 sum_j |V_j| (subnormal floor) + the bf16 rounding.
+  + 2^-16 sum_j |V_j| (subnormal floor: half of 2^-9 / 64) + the bf16 rounding.
 LSE: the row sums use unrounded probabilities, so the LSE is compared with TOL_LSE.
 """
 
@@ -101,7 +101,7 @@ def _check_vs_exact(q8, k8, v8, scales, causal, lens, scale, go):
             continue
         for h in range(q.shape[1]):
             va = np.abs(v[b, h // group, :L])
-            bound = (2.0 ** -3 * (p[b, h, :L, :L] @ va) + 2.0 ** -18 * va.sum(axis=0)
+            bound = (2.0 ** -3 * (p[b, h, :L, :L] @ va) + 2.0 ** -16 * va.sum(axis=0)
                      + 2.0 ** -8 * np.abs(ro[b, h, :L]) + 1e-6)
             err = np.abs(go[b, h, :L] - ro[b, h, :L])
             worst = max(worst, float(np.max(err / bound)))

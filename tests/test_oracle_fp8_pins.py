@@ -7,8 +7,9 @@
   three-pass oracle (itself pinned against closed forms) for any block size, causal or not,
   with padding and grouped-query heads; the LSE never depends on the rounding.
 * Closed forms: probabilities that are powers of two survive the rounding exactly; two keys
-  with probabilities 1 and 0.3 give (V0 + 0.3125 V1) / 1.3 (256 * 0.3 = 76.8 rounds to 80);
-  equal scores give the mean of V; causal row 0 returns V[0].
+  with probabilities 1 and 0.3 give (V0 + 0.3125 V1) / 1.3 (64 * 0.3 = 19.2 rounds to 20);
+  a reference that lags behind growing scores and then moves (hand-derived weights); equal
+  scores give the mean of V; causal row 0 returns V[0].
 * An error bound: the rounded result differs from the exact one by at most 2^-4 of the
   probability-weighted |V| per row (e4m3 keeps 3 mantissa bits).
 """
@@ -116,7 +117,7 @@ def test_power_of_two_probabilities_are_exact(block):
 
 @pytest.mark.parametrize("block", [1, 2])
 def test_two_keys_closed_form(block):
-    # scores 0 and ln 0.3: p = (1, 0.3); 256 * 0.3 = 76.8 -> e4m3 80 -> 0.3125
+    # scores 0 and ln 0.3: p = (1, 0.3); 64 * 0.3 = 19.2 -> e4m3 20 -> 0.3125
     e0 = np.array([1.0, 0.0, 0.0])
     q8 = _codes_of(np.broadcast_to(e0, (1, 1, 2, 3)))
     k8 = _codes_of(np.array([0.0, 1.0]).reshape(1, 1, 2, 1) * e0)
@@ -150,14 +151,14 @@ def test_rounding_error_within_e4m3_bound():
     o, _ = attention_fp8_ref(q8, k8, v8, qs, ks, vs, scale, causal=True)
     ro, _ = attention_ref(e4m3_decode(q8) * qs, e4m3_decode(k8) * ks, e4m3_decode(v8) * vs,
                           scale, causal=True)
-    # The rounding error of 256 p (p relative to a running maximum m_t <= m) is at most
-    # max(2^-4 * 256 p, 2^-10): relative 2^-4 for normals, half the subnormal spacing below.
-    # With l >= 1 this bounds |O - O_exact| by 2^-4 sum_j P_ij |V_j| + 2^-18 sum_j |V_j|.
+    # The rounding error of 64 p (p relative to the row's reference m_t <= m) is at most
+    # max(2^-4 * 64 p, 2^-10): relative 2^-4 for normals, half the subnormal spacing below.
+    # With l >= 1 this bounds |O - O_exact| by 2^-4 sum_j P_ij |V_j| + 2^-16 sum_j |V_j|.
     from oracle import attention_probs_ref
     _, _, p = attention_probs_ref(e4m3_decode(q8) * qs, e4m3_decode(k8) * ks,
                                   e4m3_decode(v8) * vs, scale, causal=True)
     vabs = np.abs(e4m3_decode(v8) * vs)
-    floor = 2.0 ** -18 * np.cumsum(vabs[0, 0], axis=0)  # causal row i sees keys 0..i
+    floor = 2.0 ** -16 * np.cumsum(vabs[0, 0], axis=0)  # causal row i sees keys 0..i
     for h in range(2):
         bound = 2.0 ** -4 * (p[0, h] @ vabs[0, 0]) + floor + 1e-12
         err = np.abs(o[0, h] - ro[0, h])
@@ -175,3 +176,26 @@ def test_row_subset_equals_full(causal, lens):
                             rows=rows)
     np.testing.assert_allclose(sub[0], full[0][:, :, rows], rtol=0, atol=1e-13)
     np.testing.assert_allclose(sub[1], full[1][:, :, rows], rtol=0, atol=1e-13)
+
+
+def test_lagging_reference_closed_form():
+    # One query, block = 1, scores (log2 units) 0, 1, 1.5, 2.5: the reference is set by key 0
+    # and stays there while scores exceed it by at most 2 (p = 1, 2, 2^1.5), then moves to 2.5.
+    # Weights before the move: 64 p = 64, 128, 181.02 -> e4m3 64, 128, 176; after it, 64.
+    e0 = np.array([1.0, 0.0])
+    s2 = np.array([0.0, 1.0, 1.5, 2.5])
+    q8 = _codes_of(np.broadcast_to(e0, (1, 1, 4, 2)))
+    k8 = _codes_of(s2.reshape(1, 1, 4, 1) * e0)           # 0, 1, 1.5, 2.5 are e4m3 values
+    rng = np.random.default_rng(38)
+    v = rng.integers(-4, 5, (4, 2)).astype(np.float64)
+    v8 = _codes_of(v.reshape(1, 1, 4, 2))
+    o, lse = attention_fp8_ref(q8, k8, v8, math.log(2.0), 1.0, 1.0, 1.0, block=1)
+    a = 2.0 ** -2.5
+    num = a * (1.0 * v[0] + 2.0 * v[1] + 2.75 * v[2]) + 1.0 * v[3]
+    den = a * (1.0 + 2.0 + 2.0 ** 1.5) + 1.0
+    np.testing.assert_allclose(o[0, 0, 3], num / den, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0, 3], math.log(np.exp2(s2).sum()), rtol=0, atol=1e-12)
+    # lag = 0 is the plain running maximum: the reference follows every new maximum
+    o0, _ = attention_fp8_ref(q8, k8, v8, math.log(2.0), 1.0, 1.0, 1.0, block=1, lag=0.0)
+    w = [2.0 ** -2.5, 2.0 ** -1.5, 2.0 ** -1.0, 1.0]      # each 64 p exact at its own reference
+    np.testing.assert_allclose(o0[0, 0, 3], (np.array(w) @ v) / sum(w), rtol=0, atol=1e-12)
