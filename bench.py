@@ -183,7 +183,7 @@ def main():
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "prefill shards by heads and decode by sequences with no exchange, so the "
               "per-GPU kernel at its share is what one GPU shows.", file=sys.stderr)
         sys.exit(2)

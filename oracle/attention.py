@@ -10,7 +10,7 @@ unfused implementation: a first pass for the row maximum, a second pass for the 
 and their sum, a third pass that normalises.  The whole N x N matrix is materialised; that is
 exactly what the fused GPU kernel avoids, and why this is slow but easy to check by eye.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
 * log-sum-exp stored per row is the natural-log LSE of the *scaled* scores,
   ``m + ln(l)`` (page "Gemini 3 Flash的注意力内核重写" §4 keeps a row maximum and a
   normaliser for the backward pass; the two are folded into one number).

@@ -2,8 +2,7 @@
 
 The pages name FP8 as the main addition of FlashAttention V3 (the "GPU优化" tag page,
 guijiagi.com, excerpt "注意力计算的性能瓶颈", part Flash Attention V3: FP8 tensor cores and an
-asynchronous pipeline on the H100) without fixing the arithmetic.  The reading taken here
-(listed in DESIGN.md):
+asynchronous pipeline on the H100) without fixing the arithmetic.  The reading taken here:
 
 * Inputs are FP8 e4m3 codes (the OCP "fn" variant: 4 exponent bits with bias 7, 3 mantissa
   bits, no infinities, max 448) with one float descale factor per tensor: the real value of a

@@ -7,7 +7,7 @@ then applies the same three-pass softmax attention as ``attention.py`` with a si
 that sees every cached token (the query is the newest token; "FlashAttention优化" §4.2.2
 describes decode as one token against the O(N d) cache).
 
-Layouts (readings listed in the design doc):
+Layouts (readings of points the pages leave open):
 * q        [S, Hq, d]
 * k_cache  [num_blocks, block_size, Hkv, d]   (token-major inside a block)
 * v_cache  same as k_cache
