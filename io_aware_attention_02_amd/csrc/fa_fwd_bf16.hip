@@ -12,9 +12,11 @@
 //
 // CDNA4 mapping (the pages' A100/H100 tile sizes are prior art, not used):
 //  * A wave owns 32 query rows; BN = 64 keys per tile.  A workgroup is 8 waves (256 rows, one
-//    workgroup per CU, two waves per SIMD) when that still gives every CU a workgroup, else 4
-//    waves (128 rows, two workgroups per CU).  A wave holds its Q^T fragments, one 64 x 32
-//    score tile and the 32 x d output accumulator in registers (<= 256 per lane).
+//    workgroup per CU, two waves per SIMD) when that still gives every CU a workgroup.  Smaller
+//    grids take 128-row workgroups: with at most one per CU, 8 waves in two key groups (each
+//    group streams every other K/V tile; the partial results are combined at the end), else 4
+//    waves, two workgroups per CU.  A wave holds its Q^T fragments, one 64 x 32 score tile and
+//    the 32 x d output accumulator in registers (<= 256 per lane).
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows are
 //    the A operand (read from LDS), Q^T the B operand (registers).  The accumulator holds one
 //    query per lane and 16 keys per lane, so row reductions are in-lane plus one exchange with
@@ -210,17 +212,27 @@ __device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* 
   return rs;
 }
 
-template <int D, bool CAUSAL, int NW, bool PAGED>
+// NG = 1: the NW waves own NW * 32 query rows and share every K/V tile.  NG = 2 (grids too
+// small to give each SIMD two waves otherwise): the waves form two groups of NW / 2 over the
+// same NW / 2 * 32 rows; group g takes the key tiles t with t % 2 == g, with its own LDS
+// buffers, and the two partial results (output, reference maximum, row sum) are combined
+// exactly at the end, as the online softmax combines any two blocks of keys
+// ("FlashAttention优化" §3.2.2).
+template <int D, bool CAUSAL, int NW, bool PAGED, int NG = 1>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(Params p) {
+  static_assert(NG == 1 || (NG == 2 && !PAGED), "key groups are for contiguous K/V");
   using G = Geo<D>;
-  constexpr int kBM = NW * kWQ;         // query rows per workgroup
+  constexpr int NWG = NW / NG;          // waves per key group
+  constexpr int kBM = NWG * kWQ;        // query rows per workgroup
   constexpr int kThreads = 64 * NW;
-  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
-  __shared__ __attribute__((aligned(1024))) char k0s[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[G::TILE];
+  constexpr int NI_W = LoadGeo<D, NWG>::NI_W;
+  // K_0, K_1, V_0, V_1: one tile per key group each (group g's at offset g * TILE).  Separate
+  // arrays, so that the compiler sees that reads of one buffer never wait for loads into another.
+  __shared__ __attribute__((aligned(1024))) char k0s[NG * G::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[NG * G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[NG * G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[NG * G::TILE];
   lds_t* const K0 = (lds_t*)k0s;
   lds_t* const K1 = (lds_t*)k1s;
   lds_t* const V0 = (lds_t*)v0s;
@@ -230,6 +242,9 @@ fwd_bf16_kernel(Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, hh = lane >> 5;
+  const int grp = NG > 1 ? __builtin_amdgcn_readfirstlane(wave / NWG) : 0;  // key group
+  const int wq = wave - grp * NWG;  // rows wq * 32 .. +31 of the workgroup's query tile
+  const int gofs = grp * G::TILE;   // the group's tile inside each buffer
 
   // Work unit = (batch, kv head): the group's query heads and their query tiles, which all read
   // the same K/V.  Each XCD runs a contiguous range of logical tiles (shared L2); when the units
@@ -276,7 +291,7 @@ fwd_bf16_kernel(Params p) {
 
   const int kv_end = CAUSAL ? min(L, off + q0 + kBM) : L;   // keys this workgroup needs
   const int n_kt = (kv_end + kBN - 1) / kBN;
-  const int qw0 = q0 + wave * kWQ;
+  const int qw0 = q0 + wq * kWQ;
   const int qrow = qw0 + c32;
   // Tiles this wave needs (fewer than n_kt on the causal diagonal; none for a paged chunk's
   // wave whose rows are all padding, common when chunks are much shorter than the query tile).
@@ -288,8 +303,8 @@ fwd_bf16_kernel(Params p) {
     tile_offsets_paged<D, NW, false>(koff, wave, lane, p.Hkv * D);
     tile_offsets_paged<D, NW, true>(voff, wave, lane, p.Hkv * D);
   } else {
-    tile_offsets<D, NW, false>(koff, wave, lane);
-    tile_offsets<D, NW, true>(voff, wave, lane);
+    tile_offsets<D, NWG, false>(koff, wq, lane);
+    tile_offsets<D, NWG, true>(voff, wq, lane);
   }
   // Paged: this wave's rows of every tile lie in one block, block `wblk` of the tile's
   // kBN / 16; its id for tile j + 1 is fetched one tile ahead (bid_next).
@@ -306,8 +321,8 @@ fwd_bf16_kernel(Params p) {
       load_tile_paged<D, NW>(Kd, p.k, bid, g, valid, p.Hkv, koff, wave);
       load_tile_paged<D, NW>(Vd, p.v, bid, g, valid, p.Hkv, voff, wave);
     } else {
-      load_tile<D, NW>(Kd, Kg, jt * kBN, L, koff, wave);
-      load_tile<D, NW>(Vd, Vg, jt * kBN, L, voff, wave);
+      load_tile<D, NWG>(Kd + gofs, Kg, jt * kBN, L, koff, wq);
+      load_tile<D, NWG>(Vd + gofs, Vg, jt * kBN, L, voff, wq);
     }
   };
 
@@ -315,8 +330,8 @@ fwd_bf16_kernel(Params p) {
   if constexpr (PAGED) {
     load_kv(K0, V0, 0, block_id(0));
     if (1 < n_kt) bid_next = block_id(1);
-  } else {
-    load_kv(K0, V0, 0, 0);
+  } else if (NG == 1 || grp < n_kt) {
+    load_kv(K0, V0, grp, 0);  // the group's first tile
   }
 
   // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel; zero for padding
@@ -327,7 +342,13 @@ fwd_bf16_kernel(Params p) {
     qf[c] = qrow < Lq ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
                       : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
-  const FragAddr<D> fa = frag_addr<D>(lane);
+  FragAddr<D> fa = frag_addr<D>(lane);
+  if constexpr (NG > 1) {
+#pragma unroll
+    for (int c = 0; c < G::KC; ++c) fa.k[c] += gofs;
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) fa.v[n] += gofs;
+  }
 
   f32x16 acc[G::NB];
 #pragma unroll
@@ -376,24 +397,29 @@ fwd_bf16_kernel(Params p) {
     }
   };
 
-  // Iteration j computes tile j from buffers j % 2 while tile j+1 loads into the others.  The
-  // buffer is fixed per instantiation, so every LDS access refers to one known buffer and the
-  // compiler never waits for the loads in flight.  Tiles [0, n_main) need no mask for any wave
-  // of the workgroup; the remaining ones (the causal diagonal, the ragged end) are masked.
+  // Iteration j computes the group's tile j * NG + grp from buffers j % 2 while its next tile
+  // loads into the others.  The buffer is fixed per instantiation, so every LDS access refers to
+  // one known buffer and the compiler never waits for the loads in flight.  Tiles [0, n_main)
+  // need no mask for any wave of the workgroup; the remaining ones (the causal diagonal, the
+  // ragged end) are masked.  Iterations are counted for the whole workgroup (n_it, one barrier
+  // each) and per wave (n_iw, the iterations whose tile the wave needs).
   const int n_main = CAUSAL ? min(off + q0, L) / kBN : L / kBN;
+  const int n_mi = n_main / NG;                  // iterations whose tiles all need no mask
+  const int n_it = (n_kt + NG - 1) / NG;
+  const int n_iw = (n_kw - grp + NG - 1) / NG;
   auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(parity)::value;
     lds_t* const Kc = ODD ? K1 : K0;
     lds_t* const Vc = ODD ? V1 : V0;
     lds_t* const Kn = ODD ? K0 : K1;
     lds_t* const Vn = ODD ? V0 : V1;
-    if (j + 1 < n_kt) {
-      load_kv(Kn, Vn, j + 1, bid_next);
+    if ((j + 1) * NG + grp < n_kt) {
+      load_kv(Kn, Vn, (j + 1) * NG + grp, bid_next);
       if constexpr (PAGED) {
         if (j + 2 < n_kt) bid_next = block_id(j + 2);
       }
     }
-    if (j < n_kw) tile(Kc, Vc, j * kBN, masked, mode);
+    if (j < n_iw) tile(Kc, Vc, (j * NG + grp) * kBN, masked, mode);
     wait_loads();
     __syncthreads();
   };
@@ -407,18 +433,18 @@ fwd_bf16_kernel(Params p) {
     // Tile 0 (K_0 and V_0 are loading or loaded): the FAST pass takes its references from it.
     wait_loads();
     __syncthreads();
-    if (0 < n_main) iter(0, even{}, unmasked{}, first_mode{});
+    if (0 < n_mi) iter(0, even{}, unmasked{}, first_mode{});
     else iter(0, even{}, masked{}, first_mode{});
     int j = 1;
-    for (; j + 1 < n_main; j += 2) {
+    for (; j + 1 < n_mi; j += 2) {
       iter(j, odd{}, unmasked{}, mode);
       iter(j + 1, even{}, unmasked{}, mode);
     }
-    if (j < n_main) {
+    if (j < n_mi) {
       iter(j, odd{}, unmasked{}, mode);
       ++j;
     }
-    for (; j < n_kt; ++j) {
+    for (; j < n_it; ++j) {
       if (j & 1) iter(j, odd{}, masked{}, mode);
       else iter(j, even{}, masked{}, mode);
     }
@@ -432,14 +458,55 @@ fwd_bf16_kernel(Params p) {
     if constexpr (PAGED) {
       load_kv(K0, V0, 0, block_id(0));
       if (1 < n_kt) bid_next = block_id(1);
-    } else {
-      load_kv(K0, V0, 0, 0);
+    } else if (NG == 1 || grp < n_kt) {
+      load_kv(K0, V0, grp, 0);
     }
     run(std::integral_constant<int, SAFE>{});
   }
 
+  float lt = add_xor32(l_run);
+  if constexpr (NG > 1) {
+    // Combine the two key groups' partial results for the same rows: group 1 hands its output
+    // accumulator, reference maximum and row sum over LDS (the tile buffers, free now) to the
+    // wave of group 0 that owns the same rows, lane for lane (the accumulator layouts match).
+    // A group whose row sum is 0 saw no key of the row and drops out; group 0 always holds the
+    // row's first key.
+    constexpr int kAccB = 64 * G::NB * 16 * 4;  // accumulator bytes per wave
+    static_assert(NWG == 4 && 2 * kAccB == NG * G::TILE, "two waves' accumulators per buffer");
+    f32x4* const xa = reinterpret_cast<f32x4*>((wq < 2 ? k0s : k1s) + (wq & 1) * kAccB);
+    float* const xm = reinterpret_cast<float*>(v0s) + wq * 128;
+    __syncthreads();  // every wave is done with the tile buffers
+    if (grp == 1) {
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = {acc[n][4 * r4], acc[n][4 * r4 + 1], acc[n][4 * r4 + 2], acc[n][4 * r4 + 3]};
+          xa[(n * 4 + r4) * 64 + lane] = v;
+        }
+      xm[lane] = m_run;
+      xm[64 + lane] = lt;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xm[lane], lt1 = xm[64 + lane];
+    const float m0 = lt > 0.f ? m_run : kNegInf;
+    const float mm = fmaxf(m0, lt1 > 0.f ? m1 : kNegInf);
+    const float a0 = lt > 0.f ? fast_exp2(m_run - mm) : 0.f;
+    const float a1 = lt1 > 0.f ? fast_exp2(m1 - mm) : 0.f;
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 v = xa[(n * 4 + r4) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[n][4 * r4 + t] = acc[n][4 * r4 + t] * a0 + v[t] * a1;
+      }
+    lt = lt * a0 + lt1 * a1;
+    m_run = mm;
+  }
+
   // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
-  const float lt = add_xor32(l_run);
   if (qrow < N) {
     const bool valid = qrow < Lq;
     const float inv = valid ? 1.f / lt : 0.f;
@@ -475,7 +542,9 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.N = a.N;
   p.sl2 = a.scale * kLog2e;
   // Eight waves (256 rows) per workgroup share each K/V tile in LDS when that still gives every
-  // CU a workgroup; otherwise four waves (128 rows), two workgroups per CU.
+  // CU a workgroup.  Otherwise 128-row workgroups: eight waves in two key groups when there are
+  // at most as many workgroups as CUs (two waves per SIMD where four waves would leave one),
+  // else four waves, two workgroups per CU.
   const long long wide = (long long)a.B * a.H * ((a.N + 8 * kWQ - 1) / (8 * kWQ));
   if (wide >= kCUs) {
     p.n_qt = (a.N + 8 * kWQ - 1) / (8 * kWQ);
@@ -484,7 +553,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   } else {
     p.n_qt = (a.N + 4 * kWQ - 1) / (4 * kWQ);
     p.total = a.B * a.H * p.n_qt;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, false>), dim3(p.total), dim3(64 * 4), 0, stream, p);
+    if (p.total <= kCUs)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8, false, 2>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, false>), dim3(p.total), dim3(64 * 4), 0, stream, p);
   }
   return hipGetLastError();
 }

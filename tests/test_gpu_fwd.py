@@ -132,15 +132,18 @@ def test_scale_zero_and_custom_scale():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_row_maximum_far_above_first_tile(causal):
+@pytest.mark.parametrize("big_key", [500, 520])
+def test_row_maximum_far_above_first_tile(causal, big_key):
     # One key of a later tile scores ~50 log2-units above every key of the first tile for every
     # query row (positive queries, a key of all 4s).  A pass that keeps the first tile's maximum
     # as the reference must notice and redo the rows exactly with the rescaling recurrence.
-    say(f"fa_fwd row maximum far above the first tile causal={causal}")
+    # Small grids split each workgroup's keys over two groups of waves (odd and even 64-key
+    # tiles): key 500 lies in an odd tile, key 520 in an even one.
+    say(f"fa_fwd row maximum far above the first tile causal={causal} key={big_key}")
     B, H, Hkv, N, d = 1, 2, 1, 1000, 128
     q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=12)
     q = q.abs()
-    k[:, :, 500] = 4.0
+    k[:, :, big_key] = 4.0
     o, lse = _run(q, k, v, causal)
     _check(q, k, v, o, lse, causal, None, 1 / d ** 0.5, TOL_O_BF16)
 
@@ -160,6 +163,25 @@ def test_wide_grid_shapes(shape):
     B, H, Hkv, N, d, causal, lens = shape
     say(f"fa_fwd wide grid {shape}")
     q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=13 + N)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    o, lse = _run(q, k, v, causal, sl)
+    _check(q, k, v, o, lse, causal, sl, 1 / d ** 0.5, TOL_O_BF16)
+
+
+# Grids between the two (fewer than one 256-row workgroup per CU, more 128-row workgroups than
+# CUs) run four-wave 128-row workgroups, two per CU.
+MID = [
+    # (B, H, Hkv, N, d, causal, lens)
+    (1, 8, 2, 5000, 128, True, [5000]),
+    (2, 4, 4, 4500, 64, False, [4500, 2100]),
+]
+
+
+@pytest.mark.parametrize("shape", MID, ids=[f"B{s[0]}H{s[1]}Hkv{s[2]}N{s[3]}d{s[4]}{'c' if s[5] else ''}" for s in MID])
+def test_mid_grid_shapes(shape):
+    B, H, Hkv, N, d, causal, lens = shape
+    say(f"fa_fwd mid grid {shape}")
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=15 + N)
     sl = torch.tensor(lens, dtype=torch.int32)
     o, lse = _run(q, k, v, causal, sl)
     _check(q, k, v, o, lse, causal, sl, 1 / d ** 0.5, TOL_O_BF16)
