@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,fwd_fp8,bwd,prefill_paged,decode,copy} [--steps K]
+    python bench.py --only {fwd,fwd_causal,fwd_gqa,fwd_fp8,bwd,prefill_paged,decode,copy} [--steps K]
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -118,6 +118,16 @@ def only(args, torch, dev, wf, wd):
         causal = args.only == "fwd_causal"
         fn = lambda: fa_fwd(q, k, v, o, lse, causal=causal)  # noqa: E731
         what = f"fa_fwd B=1 H=8 N=16384 d=128 bf16 causal={causal}"
+    elif args.only == "fwd_gqa":
+        from io_aware_attention_02_amd.inputs import WORKLOADS
+        w4 = WORKLOADS["gqa_varlen_8k"]
+        q, k, v, lens = prefill_inputs(w4["B"], w4["H"], w4["Hkv"], w4["N"], w4["d"], "bf16",
+                                       seed=w4["seed"], len_lo=w4["len_lo"], len_hi=w4["len_hi"])
+        what = (f"fa_fwd B=4 Hq=32 Hkv=8 N=8192 d=128 bf16 causal, seq_lens={lens.tolist()}")
+        q, k, v, lens = q.to(dev), k.to(dev), v.to(dev), lens.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fn = lambda: fa_fwd(q, k, v, o, lse, causal=True, seq_lens=lens)  # noqa: E731
     elif args.only == "fwd_fp8":
         from io_aware_attention_02_amd import fa_fwd_fp8
         from io_aware_attention_02_amd.inputs import WORKLOADS, fp8_inputs
@@ -177,8 +187,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_fp8", "bwd", "prefill_paged",
-                                       "decode", "copy"],
+    ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_gqa", "fwd_fp8", "bwd",
+                                       "prefill_paged", "decode", "copy"],
                     default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()

@@ -209,8 +209,10 @@ bwd_dq_kernel(BwdParams p) {
   int unit, rem;
   unit_of(p, p.group * p.n_t, unit, rem);
   const int b = unit / p.Hkv, g = unit - b * p.Hkv;
-  const int hi = rem / p.n_t;
-  int qt = rem - hi * p.n_t;
+  // The group's query heads take consecutive slots for each query tile (same K/V rows side by
+  // side, every head's heaviest tiles first).
+  int qt = rem / p.group;
+  const int hi = rem - qt * p.group;
   if (CAUSAL) qt = p.n_t - 1 - qt;  // heaviest query tiles first
   const int N = p.N, h = g * p.group + hi;
   const int bh = b * p.H + h;

@@ -259,8 +259,11 @@ fwd_bf16_kernel(Params p) {
   int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
   if (PAGED || p.seq_lens != nullptr) b = by_work<NW, PAGED>(p, b, rank_buf);  // heaviest first
-  const int hi = rem / p.n_qt;
-  int qt = rem - hi * p.n_qt;
+  // Inside a unit the group's query heads take consecutive slots for each query tile: heads that
+  // read the same K/V rows run side by side (shared L2 lines), and every head's heaviest tiles
+  // come before any head's lighter ones.
+  int qt = rem / p.group;
+  const int hi = rem - qt * p.group;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
   const int H = p.H, N = p.N;
   const int h = g * p.group + hi;

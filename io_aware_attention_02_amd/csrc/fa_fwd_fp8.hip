@@ -161,8 +161,10 @@ fwd_fp8_kernel(Params8 p) {
   const int rem = lam - unit * per_unit;
   if (units % kXcds8 == 0) unit = (unit % (units / kXcds8)) * kXcds8 + unit / (units / kXcds8);
   const int b = unit / p.Hkv, g = unit - b * p.Hkv;
-  const int hi = rem / p.n_qt;
-  int qt = rem - hi * p.n_qt;
+  // The group's query heads take consecutive slots for each query tile (same K/V rows side by
+  // side, every head's heaviest tiles first).
+  int qt = rem / p.group;
+  const int hi = rem - qt * p.group;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
   const int N = p.N;
   const int h = g * p.group + hi;
