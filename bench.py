@@ -101,7 +101,47 @@ def cpu_baseline(prefill_inputs, w, budget_s=10.0):
         "sample": f"fp64 three-pass oracle on {done} blocks of {R} query rows (head-major, "
                   f"head 0 first) x {N} keys, d={d}, {elapsed:.1f} s; flops counted as 4*rows*N*d "
                   f"like the GPU figure",
+        "small_workloads": oracle_small_workloads(prefill_inputs),
     }
+
+
+def oracle_small_workloads(prefill_inputs, repeats=3):
+    """The fp64 oracle over the two small workloads in full (single-head fp32 N=256 d=64, and
+    B=1 H=8 N=4096 d=128), on one thread and on all host cores: median wall seconds of
+    `repeats` runs, input generation excluded."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from io_aware_attention_02_amd.inputs import WORKLOADS
+    from oracle import attention_ref
+
+    all_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    res = {"cpu": _cpu_model(), "all_threads": int(all_threads)}
+    for name in ("single_head_fp32", "prefill_4k"):
+        w = WORKLOADS[name]
+        q, k, v, _ = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], w["dtype"],
+                                    seed=w["seed"])
+        qf, kf, vf = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+        for label, limit in (("1_thread", 1), ("all_threads", all_threads)):
+            times = []
+            with threadpool_limits(limits=limit):
+                for _ in range(repeats):
+                    t0 = time.perf_counter()
+                    attention_ref(qf, kf, vf, 1 / math.sqrt(w["d"]))
+                    times.append(time.perf_counter() - t0)
+            res[f"{name}_{label}_s"] = round(sorted(times)[len(times) // 2], 4)
+    return res
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def only(args, torch, dev, wf, wd):
