@@ -263,9 +263,8 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
   if (Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
   // Grid: one 64-thread workgroup per (kv head, key range of 512 tokens, sequence), rounded up
   // to a multiple of 8 ranges; the total thread count must fit a 32-bit grid.
-  const long long splits =
-      ((long long)max_blocks_per_seq * block_size + fa::kDecodeSplitTokens - 1) /
-      fa::kDecodeSplitTokens;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return FA_ERR_UNSUPPORTED;
+  const long long splits = fa::decode_splits(max_blocks_per_seq, block_size);
   const long long units = ((long long)num_seqs * splits + 7) / 8 * 8;
   if (units * Hkv * 64 > INT_MAX) return FA_ERR_UNSUPPORTED;
   const size_t need =

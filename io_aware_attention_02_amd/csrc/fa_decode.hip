@@ -359,10 +359,6 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeParams p) {
     p.lse[(size_t)b * p.Hq + h] = (M + __log2f(den)) * kLn2;
 }
 
-int max_splits(int max_blocks, int block_size) {
-  const long long tokens = (long long)max_blocks * block_size;
-  return (int)((tokens + kSplit - 1) / kSplit);
-}
 
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
@@ -379,7 +375,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.group = a.Hq / a.Hkv;
   p.max_blocks = a.max_blocks;
   p.max_tokens = a.max_blocks * a.block_size;
-  p.MS = max_splits(a.max_blocks, a.block_size);
+  p.MS = decode_splits(a.max_blocks, a.block_size);
   const size_t slots = (size_t)a.S * a.Hq * p.MS;
   p.opart = static_cast<float*>(a.workspace);
   p.mpart = p.opart + slots * D;
@@ -396,9 +392,23 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Key ranges per sequence in the split grid (the workspace holds one partial result per range):
+// ceil(max tokens / 512), raised to 7 mod 8 once there are at least 8.  Work unit u = b * MS + sp
+// runs on XCD u mod 8 (workgroups are dealt round-robin over the XCDs), so with MS = 7 mod 8,
+// range sp of sequence b lands on XCD (sp - b) mod 8: each sequence starts on a different XCD,
+// and the ranges left over after whole rounds of 8 (and the empty ones past a short sequence's
+// end) spread over all XCDs instead of piling onto the low-numbered ones.  The added ranges are
+// empty and exit at once.
+int decode_splits(int max_blocks, int block_size) {
+  const long long tokens = (long long)max_blocks * block_size;
+  int ms = (int)((tokens + kSplit - 1) / kSplit);
+  if (ms >= kXcds) ms += kXcds - 1 - ms % kXcds;
+  return ms;
+}
+
 size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size) {
   if (S <= 0 || Hq <= 0 || d <= 0 || max_blocks <= 0 || block_size <= 0) return 0;
-  const size_t slots = (size_t)S * Hq * max_splits(max_blocks, block_size);
+  const size_t slots = (size_t)S * Hq * decode_splits(max_blocks, block_size);
   return slots * ((size_t)d + 2) * sizeof(float);
 }
 

@@ -101,8 +101,10 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
-// Tokens per key-range split of the decode kernel and the resulting workspace size.
+// Tokens per key-range split of the decode kernel, key ranges per sequence in its grid, and the
+// resulting workspace size.
 constexpr int kDecodeSplitTokens = 512;
+int decode_splits(int max_blocks, int block_size);
 size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -54,7 +54,10 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     # 64 sequences x 32 heads x ceil(2048*16/512)=64 ranges x (128 + 2) floats
-    assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 2048, 16) == 64 * 32 * 64 * 130 * 4
+    # 32768 tokens = 64 ranges of 512, raised to 71 (7 mod 8) so ranges spread over the 8 XCDs
+    assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 2048, 16) == 64 * 32 * 71 * 130 * 4
+    assert lib.fa_paged_decode_workspace_bytes(2, 1, 128, 224, 16) == 2 * 7 * 130 * 4   # 7 ranges
+    assert lib.fa_paged_decode_workspace_bytes(2, 1, 128, 256, 16) == 2 * 15 * 130 * 4  # 8 -> 15
     assert lib.fa_paged_decode_workspace_bytes(1, 1, 64, 1, 16) == 66 * 4
     assert lib.fa_paged_decode_workspace_bytes(0, 32, 128, 2048, 16) == 0
     assert lib.fa_paged_decode_workspace_bytes(4, 32, 128, -1, 16) == 0
