@@ -102,3 +102,19 @@ def test_paged_decode_workload():
                                                w["len_lo"], w["len_hi"], seed=w["seed"])
     o, lse = _run(q, kc, vc, table, sl)
     _check(q, kc, vc, table, sl, o, lse, 1 / 128 ** 0.5)
+
+
+@pytest.mark.parametrize("max_blocks", [255, 256, 512])
+def test_decode_range_counts_around_the_xcd_padding(max_blocks):
+    # 255 blocks = 8 ranges of 512 tokens (raised to 15 per sequence), 256 = 8 (15), 512 = 16
+    # (23): sequences of every length up to the table's capacity, empty ones included.
+    S = 40
+    lens = [0] + [int(x) for x in np.linspace(1, max_blocks * 16, S - 1)]
+    say(f"fa_paged_decode {S} seqs, block table of {max_blocks} blocks, lens 0..{max_blocks * 16}")
+    q, kc, vc, table, sl = paged_decode_inputs(S, 16, 4, 128, 16, seed=330 + max_blocks,
+                                               seq_lens=lens)
+    if table.shape[1] < max_blocks:  # widen the table to the capacity under test (unused: -1)
+        pad = torch.full((S, max_blocks - table.shape[1]), -1, dtype=torch.int32)
+        table = torch.cat([table, pad], dim=1)
+    o, lse = _run(q, kc, vc, table, sl)
+    _check(q, kc, vc, table, sl, o, lse, 1 / 128 ** 0.5)
