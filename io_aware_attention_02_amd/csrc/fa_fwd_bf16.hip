@@ -107,27 +107,23 @@ __device__ __forceinline__ void load_tile_paged(lds_t* dst, const bf16* cache, i
 }
 
 // With per-sequence lengths (varlen prefill, paged chunked prefill): the sequence a workgroup
-// serves, taken in order of decreasing work (key length times query rows, ties by index), so
-// that the longest sequences start first and the short ones fill in behind them.  Every
-// workgroup ranks the sequences itself, one thread per sequence against lengths staged in LDS;
-// with more than kMaxRanked sequences the natural order is kept.  The order changes no result.
+// serves, taken in order of decreasing key length L (ties by index).  A workgroup's cost grows
+// with the keys its rows see, up to L, so the sequences holding the heaviest workgroups start
+// first and the light ones fill in behind them.  (Ranking by a sequence's total work, L times its
+// query rows, would put a long context with a short chunk -- one very heavy workgroup -- near
+// the end of the grid.)  For the contiguous forward the query rows are the keys, so this is also
+// the order of total work.  Every workgroup ranks the sequences itself, one thread per sequence
+// against lengths staged in LDS; with more than kMaxRanked sequences the natural order is kept.
+// The order changes no result.
 constexpr int kMaxRanked = 512;
 template <int NW, bool PAGED>
 __device__ int by_work(const Params& p, int pos, int* buf) {
   const int S = p.total / (p.H * p.n_qt);
   if (S > kMaxRanked) return pos;
-  int* w = buf;                   // work of each sequence, saturated to 31 bits
+  int* w = buf;                   // key length of each sequence
   int* order = buf + kMaxRanked;  // sequence at each rank
-  for (int i = threadIdx.x; i < S; i += 64 * NW) {
-    int L, Q;
-    if constexpr (PAGED) {
-      L = min(max(p.seq_lens[i], 0), p.max_blocks * kPageRows);
-      Q = min(max(p.q_lens[i], 0), min(L, p.N));
-    } else {
-      L = Q = min(max(p.seq_lens[i], 0), p.N);
-    }
-    w[i] = (int)min((long long)L * Q, (long long)0x7fffffff);
-  }
+  for (int i = threadIdx.x; i < S; i += 64 * NW)
+    w[i] = min(max(p.seq_lens[i], 0), PAGED ? p.max_blocks * kPageRows : p.N);
   __syncthreads();
   for (int i = threadIdx.x; i < S; i += 64 * NW) {
     int r = 0;
