@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,fwd_gqa,fwd_fp8,bwd,prefill_paged,decode,copy} [--steps K]
+    python bench.py --only {fwd,fwd_causal,fwd_4k,fwd_gqa,fwd_fp8,bwd,prefill_paged,decode,copy} [--steps K]
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -158,6 +158,16 @@ def only(args, torch, dev, wf, wd):
         causal = args.only == "fwd_causal"
         fn = lambda: fa_fwd(q, k, v, o, lse, causal=causal)  # noqa: E731
         what = f"fa_fwd B=1 H=8 N=16384 d=128 bf16 causal={causal}"
+    elif args.only == "fwd_4k":
+        from io_aware_attention_02_amd.inputs import WORKLOADS
+        w2 = WORKLOADS["prefill_4k"]
+        q, k, v, _ = prefill_inputs(w2["B"], w2["H"], w2["Hkv"], w2["N"], w2["d"], "bf16",
+                                    seed=w2["seed"])
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fn = lambda: fa_fwd(q, k, v, o, lse)  # noqa: E731
+        what = "fa_fwd B=1 H=8 N=4096 d=128 bf16 non-causal"
     elif args.only == "fwd_gqa":
         from io_aware_attention_02_amd.inputs import WORKLOADS
         w4 = WORKLOADS["gqa_varlen_8k"]
@@ -227,7 +237,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_gqa", "fwd_fp8", "bwd",
+    ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_4k", "fwd_gqa", "fwd_fp8", "bwd",
                                        "prefill_paged", "decode", "copy"],
                     default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
