@@ -95,11 +95,13 @@ def test_decode_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_paged_decode_workload():
+@pytest.mark.parametrize("seed", [None, 101, 102, 103])  # the workload's own seed, then repeats
+def test_paged_decode_workload(seed):
     w = WORKLOADS["paged_decode"]
-    say("fa_paged_decode 64 seqs Hq=32 Hkv=8 d=128 lens U[512,32768] (every sequence)")
+    seed = w["seed"] if seed is None else seed
+    say(f"fa_paged_decode 64 seqs Hq=32 Hkv=8 d=128 lens U[512,32768] (every sequence), seed {seed}")
     q, kc, vc, table, sl = paged_decode_inputs(w["S"], w["Hq"], w["Hkv"], w["d"], w["block_size"],
-                                               w["len_lo"], w["len_hi"], seed=w["seed"])
+                                               w["len_lo"], w["len_hi"], seed=seed)
     o, lse = _run(q, kc, vc, table, sl)
     _check(q, kc, vc, table, sl, o, lse, 1 / 128 ** 0.5)
 

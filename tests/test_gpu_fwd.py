@@ -217,10 +217,12 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_prefill_4k_workload_full():
+@pytest.mark.parametrize("seed", [None, 101, 102, 103])  # the workload's own seed, then repeats
+def test_prefill_4k_workload_full(seed):
     w = WORKLOADS["prefill_4k"]
-    say("fa_fwd B=1 H=8 N=4096 d=128 bf16, every row")
-    q, k, v, _ = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], "bf16", seed=w["seed"])
+    seed = w["seed"] if seed is None else seed
+    say(f"fa_fwd B=1 H=8 N=4096 d=128 bf16, every row, seed {seed}")
+    q, k, v, _ = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], "bf16", seed=seed)
     o, lse = _run(q, k, v, False)
     _check(q, k, v, o, lse, False, None, 1 / 128 ** 0.5, TOL_O_BF16)
 
