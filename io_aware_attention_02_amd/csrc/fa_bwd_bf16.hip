@@ -349,7 +349,7 @@ constexpr int kQBuf = 3;  // query tile buffers
 __device__ __forceinline__ void load_stats(lds_t* dst, const float* rowbase, int row0, int L,
                                            int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const int bytes = __builtin_amdgcn_readfirstlane(max(L - row0, 0) * 4);
+  const int bytes = __builtin_amdgcn_readfirstlane(min(max(L - row0, 0), 64) * 4);  // one tile
   const uintptr_t base = reinterpret_cast<uintptr_t>(rowbase + row0);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));

@@ -112,13 +112,14 @@ __device__ __forceinline__ void tile_offsets8(int* off, int wave, int lane, bool
 }
 
 // Direct global -> LDS copy of one tile (rows key0 .. key0 + 127); rows at or past L read zero.
+// The resource size stops at the tile's end, so it cannot overflow for long sequences.
 template <int D, int NW>
 __device__ __forceinline__ void load_tile8(lds8_t* dst, const uint8_t* head, int key0, int L,
                                            const int* off, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = Geo8<D>;
   constexpr int NI_W = G::NI / NW;
-  const int bytes = __builtin_amdgcn_readfirstlane(max(L - key0, 0) * G::RB);
+  const int bytes = __builtin_amdgcn_readfirstlane(min(max(L - key0, 0), kBN8) * G::RB);
   const uintptr_t base = reinterpret_cast<uintptr_t>(head + (size_t)key0 * D);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));

@@ -66,9 +66,10 @@ __device__ __forceinline__ void tile_offsets(int* off, int wave, int lane) {
 }
 
 // Direct global -> LDS copy of one K or V tile (rows key0 .. key0+BN-1) through a buffer
-// resource whose base is the tile's first row and whose size ends at the valid length L: rows
-// at or past L are out of range and arrive as zeros (their scores are masked, so they add
-// exactly nothing), and no load can leave the tensor.
+// resource whose base is the tile's first row and whose size ends at the valid length L or at
+// the tile's end, whichever comes first: rows at or past L are out of range and arrive as zeros
+// (their scores are masked, so they add exactly nothing), no load can leave the tensor, and the
+// 32-bit size cannot overflow however long the sequence.
 template <int D, int NW>
 __device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0, int L,
                                           const int* off, int wave) {
@@ -77,7 +78,7 @@ __device__ __forceinline__ void load_tile(lds_t* dst, const bf16* head, int key0
   constexpr int NI_W = LoadGeo<D, NW>::NI_W;
   // The tile's base and size are the same for every lane; readfirstlane states it so the
   // resource stays in scalar registers.
-  const int bytes = __builtin_amdgcn_readfirstlane(max(L - key0, 0) * G::RB);
+  const int bytes = __builtin_amdgcn_readfirstlane(min(max(L - key0, 0), kBN) * G::RB);
   const uintptr_t base = reinterpret_cast<uintptr_t>(head + (size_t)key0 * D);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
