@@ -98,10 +98,11 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * Q = q_scale * e4m3(q) and likewise K, V.  Computes O = softmax(scale * Q K^T) V and the LSE
  * as fa_fwd does, with these differences in arithmetic:
  *   - both products run on the FP8 matrix cores with fp32 accumulation;
- *   - the softmax runs over blocks of 64 keys with a running row maximum m (the online
- *     recurrence of "FlashAttention优化" §3.2.1); the probabilities exp(S - m) of a block enter
- *     the P V product rounded to e4m3 after a factor 256 (relative error at most 2^-4 each),
- *     while the row sum and the LSE use them unrounded.
+ *   - the softmax runs over blocks of 64 keys with the online recurrence of
+ *     "FlashAttention优化" §3.2.1, where each row's reference m moves to a block's maximum only
+ *     when that maximum exceeds it by more than a factor 2^2 (so exp(S - m) <= 4); the
+ *     probabilities of a block enter the P V product as e4m3(64 p) / 64 (relative error at most
+ *     2^-4 each), while the row sum and the LSE use them unrounded.
  *
  *   q         [B, H, N, d] e4m3 codes (1 byte each)
  *   k, v      [B, Hkv, N, d] e4m3 codes
