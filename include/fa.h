@@ -63,8 +63,10 @@ enum { FA_BF16 = 0, /* bf16 storage, fp32 arithmetic and accumulation on the mat
  * algorithm part, with the scale passed explicitly (1/sqrt(d) for the standard layer).  The
  * kernel follows the fused, tiled scheme of "Gemini 3 Flash的注意力内核重写：算子融合如何实现
  * 亚毫秒级推理" (sections on kernel fusion, tiling and the online softmax) and the running
- * statistics of "FlashAttention优化" §3.2.1: a running row maximum m and row sum l, rescaled
- * whenever m grows, the output normalised once at the end.
+ * statistics of "FlashAttention优化" §3.2.1: a row maximum m and row sum l, the output
+ * normalised once at the end.  (Each row's reference m is taken from its first key tile and kept;
+ * a workgroup in which some later probability could exceed 2^16 recomputes with the running
+ * maximum and rescaling of §3.2.1.  Both give the same softmax.)
  *
  *   q         [B, H, N, d]    element type `dtype`
  *   k, v      [B, Hkv, N, d]  element type `dtype`
