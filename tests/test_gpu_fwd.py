@@ -187,6 +187,20 @@ def test_mid_grid_shapes(shape):
     _check(q, k, v, o, lse, causal, sl, 1 / d ** 0.5, TOL_O_BF16)
 
 
+def test_mid_grid_row_maximum_far_above_first_tile():
+    # The four-wave 128-row kernel (two workgroups per CU) with per-sequence lengths takes the
+    # exact fallback pass too; the big key is visible to the longer sequence only.
+    say("fa_fwd mid grid, row maximum far above the first tile")
+    B, H, Hkv, N, d = 2, 4, 2, 4600, 128
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=16)
+    q = q.abs()
+    k[:, :, 3000] = 4.0
+    sl = torch.tensor([4600, 2500], dtype=torch.int32)
+    for causal in (False, True):
+        o, lse = _run(q, k, v, causal, sl)
+        _check(q, k, v, o, lse, causal, sl, 1 / d ** 0.5, TOL_O_BF16)
+
+
 def test_wide_grid_row_maximum_far_above_first_tile():
     say("fa_fwd wide grid, row maximum far above the first tile")
     B, H, Hkv, N, d = 2, 32, 8, 1000, 128

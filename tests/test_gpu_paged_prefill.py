@@ -113,3 +113,19 @@ def test_paged_prefill_workload_sampled_sequences():
     small = sorted(range(w["S"]), key=lambda b: int(sl[b]) * int(ql[b]))[:3]
     _check(q, kc, vc, table, sl, ql, o, lse, 1 / w["d"] ** 0.5, seqs=small)
     assert torch.isfinite(o.float()).all()
+
+
+def test_paged_prefill_row_maximum_far_above_first_tile():
+    # One cached token scores ~50 log2-units above every token of each row's first key tile
+    # (positive queries, that token's keys all 4): the paged instantiation must take the exact
+    # fallback pass, re-gathering its blocks through the table.
+    S, Hq, Hkv, d, Q = 2, 8, 2, 128, 200
+    lens, qls = [3000, 900], [200, 150]
+    say("fa_paged_prefill row maximum far above the first tile")
+    q, kc, vc, table, sl, ql = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=312, seq_lens=lens,
+                                                    q_lens=qls)
+    q = q.abs()
+    for b, t in ((0, 1700), (1, 500)):  # tokens before each chunk, visible to all its rows
+        kc[int(table[b, t // 16]), t % 16] = 4.0
+    o, lse = _run(q, kc, vc, table, sl, ql)
+    _check(q, kc, vc, table, sl, ql, o, lse, 1 / d ** 0.5)
