@@ -306,12 +306,15 @@ fwd_bf16_kernel(Params p) {
     tile_offsets<D, NWG, true>(voff, wq, lane);
   }
   // Paged: this wave's rows of every tile lie in one block, block `wblk` of the tile's
-  // kBN / 16; its id for tile j + 1 is fetched one tile ahead (bid_next).
-  const int wblk = wave * NI_W * G::RPI / kPageRows;
+  // kBN / 16; its id for tile j + 1 is fetched one tile ahead (bid_next).  The id is read by a
+  // scalar load (the table is read-only for the kernel's lifetime and the address is uniform):
+  // a vector load would be waited for through the vector-memory counter, which retires in
+  // order, so that wait would also drain the tile loads issued just before it.
+  const int wblk = __builtin_amdgcn_readfirstlane(wave * NI_W * G::RPI / kPageRows);
   const int* trow = PAGED ? p.table + (size_t)b * p.max_blocks : nullptr;
   auto block_id = [&](int jt) __attribute__((always_inline)) {
     const int blk = jt * (kBN / kPageRows) + wblk;
-    return blk * kPageRows < L ? __builtin_amdgcn_readfirstlane(trow[blk]) : 0;
+    return blk * kPageRows < L ? *(const __attribute__((address_space(4))) int*)(trow + blk) : 0;
   };
   int bid_next = 0;
   auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt, int bid) __attribute__((always_inline)) {
