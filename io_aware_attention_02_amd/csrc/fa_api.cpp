@@ -261,7 +261,7 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (block_size != 16) return FA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
-  // Grid: one 64-thread workgroup per (kv head, key range of 512 tokens, sequence), rounded up
+  // Grid: one 64-thread workgroup per (kv head, key range, sequence), at most one per 512 tokens, rounded up
   // to a multiple of 8 ranges; the total thread count must fit a 32-bit grid.
   if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return FA_ERR_UNSUPPORTED;
   const long long splits = fa::decode_splits(max_blocks_per_seq, block_size);

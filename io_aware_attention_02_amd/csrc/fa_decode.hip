@@ -10,8 +10,9 @@
 //  * §二.4 -- gather and attention are one kernel: scores against the register-resident query,
 //    online softmax and the probability-weighted sum of values follow each gathered block.
 // Load balance (§二.2 asks for dynamic balancing of unequal per-query work): instead of a
-// per-warp task queue, each sequence's tokens are cut into fixed 512-token ranges, one wave
-// each, so work per wave is equal whatever the length mix.  Each range writes its partial
+// per-warp task queue, each sequence's tokens are cut into fixed-length ranges (512 tokens, or
+// 1024 when the grid is large enough to fill the chip with them), one wave each, so work per wave
+// is equal whatever the length mix.  Each range writes its partial
 // (max, sum, unnormalised output); a second kernel merges them exactly with the rescaling
 // rule of the online softmax ("FlashAttention优化" §3.2.2: the result is the same for any
 // block order and grouping).
@@ -40,8 +41,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kBS = 16;                         // tokens per physical block
-constexpr int kSplit = kDecodeSplitTokens;      // tokens per wave
-constexpr int kBlocksPerSplit = kSplit / kBS;   // block ids prefetched per wave (<= 64)
+constexpr int kSplit = kDecodeSplitTokens;      // tokens per wave, short grids
+constexpr int kLongSplit = kDecodeLongSplitTokens;  // tokens per wave, long grids
+constexpr int kBlocksPerSplit = kLongSplit / kBS;  // block ids prefetched per wave (<= 64)
 constexpr int kStages = 4;                      // blocks in the load ring
 constexpr int kBufferFlags = 0x00020000;        // buffer resource word 3: 32-bit data, raw
 constexpr int kXcds = 8;                        // accelerator complex dies (each with its own L2)
@@ -62,6 +64,7 @@ struct DecodeParams {
   float* mpart;  // [S][Hq][MS]
   float* lpart;  // [S][Hq][MS]
   int Hq, Hkv, group, max_blocks, max_tokens, MS, units;
+  int split;  // tokens per key range: kSplit or kLongSplit
   float sl2;
 };
 
@@ -150,9 +153,9 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
   if (u >= p.units) return;
   const int b = u / p.MS, sp = u - b * p.MS;
   const int L = min(max(p.lens[b], 0), p.max_tokens);
-  const int tok_begin = sp * kSplit;
+  const int tok_begin = sp * p.split;
   if (tok_begin >= L) return;
-  const int tok_end = min(L, tok_begin + kSplit);
+  const int tok_end = min(L, tok_begin + p.split);
   const int blk_begin = tok_begin / kBS;
   const int n_blk = (tok_end - tok_begin + kBS - 1) / kBS;
 
@@ -297,7 +300,7 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = min(max(p.lens[b], 0), p.max_tokens);
-  const int n = (L + kSplit - 1) / kSplit;
+  const int n = (L + p.split - 1) / p.split;
   const size_t base = ((size_t)b * p.Hq + h) * p.MS;
   bf16* out = p.o + ((size_t)b * p.Hq + h) * D + lane * DPL;
   if (n == 0) {
@@ -375,7 +378,14 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.group = a.Hq / a.Hkv;
   p.max_blocks = a.max_blocks;
   p.max_tokens = a.max_blocks * a.block_size;
-  p.MS = decode_splits(a.max_blocks, a.block_size);
+  // Range length: 1024 tokens when the grid still holds enough waves for that (fewer partial
+  // results, and each wave's load ramp is paid over twice the tokens), else 512 so that short
+  // contexts still fill the chip.  Measured: 64 sequences U[512, 32768] 0.684 -> 0.667 ms,
+  // 256 U[512, 8192] 0.807 -> 0.784 ms; 64 U[512, 4096] would go 0.127 -> 0.148 ms and keeps 512.
+  const long long long_waves = (long long)a.S * a.Hkv *
+      ((p.max_tokens + (long long)kLongSplit - 1) / kLongSplit);
+  p.split = long_waves >= kLongSplitMinWaves ? kLongSplit : kSplit;
+  p.MS = decode_splits_of(a.max_blocks, a.block_size, p.split);
   const size_t slots = (size_t)a.S * a.Hq * p.MS;
   p.opart = static_cast<float*>(a.workspace);
   p.mpart = p.opart + slots * D;
@@ -393,17 +403,23 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Key ranges per sequence in the split grid (the workspace holds one partial result per range):
-// ceil(max tokens / 512), raised to 7 mod 8 once there are at least 8.  Work unit u = b * MS + sp
+// ceil(max tokens / range length), raised to 7 mod 8 once there are at least 8.  Work unit u = b * MS + sp
 // runs on XCD u mod 8 (workgroups are dealt round-robin over the XCDs), so with MS = 7 mod 8,
 // range sp of sequence b lands on XCD (sp - b) mod 8: each sequence starts on a different XCD,
 // and the ranges left over after whole rounds of 8 (and the empty ones past a short sequence's
 // end) spread over all XCDs instead of piling onto the low-numbered ones.  The added ranges are
 // empty and exit at once.
-int decode_splits(int max_blocks, int block_size) {
+int decode_splits_of(int max_blocks, int block_size, int split) {
   const long long tokens = (long long)max_blocks * block_size;
-  int ms = (int)((tokens + kSplit - 1) / kSplit);
+  int ms = (int)((tokens + split - 1) / split);
   if (ms >= kXcds) ms += kXcds - 1 - ms % kXcds;
   return ms;
+}
+
+// The 512-token count bounds the 1024-token one (both steps are monotone in the token count), so
+// the workspace and the grid-size check use it whichever length the launch picks.
+int decode_splits(int max_blocks, int block_size) {
+  return decode_splits_of(max_blocks, block_size, kSplit);
 }
 
 size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size) {

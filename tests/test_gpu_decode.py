@@ -120,3 +120,19 @@ def test_decode_range_counts_around_the_xcd_padding(max_blocks):
         table = torch.cat([table, pad], dim=1)
     o, lse = _run(q, kc, vc, table, sl)
     _check(q, kc, vc, table, sl, o, lse, 1 / 128 ** 0.5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_1024_token_ranges_ragged(d):
+    # A block table 2048 blocks wide for 64 sequences and 8 kv heads puts 64 * 8 * 32 = 16384
+    # waves in a grid of 1024-token ranges, enough for the launch to take that range length; the
+    # lengths sit around its edges (and the 512-token ones), with one empty sequence and one at
+    # the table's capacity.  The other sequences stay short so that the cache stays small.
+    S = 64
+    edge = [0, 1, 15, 16, 17, 511, 512, 513, 1023, 1024, 1025, 2047, 2048, 2049, 3073, 32768]
+    lens = edge + [int(x) for x in np.linspace(2, 3000, S - len(edge))]
+    say(f"fa_paged_decode d={d} {S} seqs, block table of 2048 blocks, 1024-token ranges, lens {edge} + short")
+    q, kc, vc, table, sl = paged_decode_inputs(S, 32, 8, d, 16, seed=360 + d, seq_lens=lens)
+    assert table.shape[1] == 2048
+    o, lse = _run(q, kc, vc, table, sl)
+    _check(q, kc, vc, table, sl, o, lse, 1 / d ** 0.5)
