@@ -109,7 +109,9 @@ def test_paged_decode_workload(seed):
 @pytest.mark.parametrize("max_blocks", [255, 256, 512])
 def test_decode_range_counts_around_the_xcd_padding(max_blocks):
     # 255 blocks = 8 ranges of 512 tokens (raised to 15 per sequence), 256 = 8 (15), 512 = 16
-    # (23): sequences of every length up to the table's capacity, empty ones included.
+    # (23): sequences of every length up to the table's capacity, empty ones included.  With 40
+    # sequences and 4 kv heads the grid is too small for 1024-token ranges (at most 40 * 4 * 8 =
+    # 1280 waves), so this covers the 512-token path; the 1024-token one is tested below.
     S = 40
     lens = [0] + [int(x) for x in np.linspace(1, max_blocks * 16, S - 1)]
     say(f"fa_paged_decode {S} seqs, block table of {max_blocks} blocks, lens 0..{max_blocks * 16}")
