@@ -378,13 +378,16 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.group = a.Hq / a.Hkv;
   p.max_blocks = a.max_blocks;
   p.max_tokens = a.max_blocks * a.block_size;
-  // Range length: 1024 tokens when the grid still holds enough waves for that (fewer partial
-  // results, and each wave's load ramp is paid over twice the tokens), else 512 so that short
-  // contexts still fill the chip.  Measured: 64 sequences U[512, 32768] 0.684 -> 0.667 ms,
-  // 256 U[512, 8192] 0.807 -> 0.784 ms; 64 U[512, 4096] would go 0.127 -> 0.148 ms and keeps 512.
-  const long long long_waves = (long long)a.S * a.Hkv *
-      ((p.max_tokens + (long long)kLongSplit - 1) / kLongSplit);
-  p.split = long_waves >= kLongSplitMinWaves ? kLongSplit : kSplit;
+  // Range length: 1024 tokens when a full-length sequence still has at least 8 ranges and the
+  // grid at least four rounds of waves (fewer partial results, and each wave's load ramp is paid
+  // over twice the tokens), else 512: short contexts cut into 1024-token ranges leave a ragged
+  // last round.  Measured, 512 -> 1024: 64 sequences U[512, 32768] 0.684 -> 0.667 ms, 32 such
+  // 0.378 -> 0.372, 48 U[512, 16384] 0.311 -> 0.306, 256 U[512, 8192] 0.807 -> 0.784; but
+  // 64 U[512, 4096] 0.127 -> 0.148 and 128 U[512, 4096] 0.218 -> 0.267, which keep 512.
+  const long long long_ranges = (p.max_tokens + (long long)kLongSplit - 1) / kLongSplit;
+  const long long long_waves = (long long)a.S * a.Hkv * long_ranges;
+  p.split = (long_ranges >= kLongSplitMinRanges && long_waves >= kLongSplitMinWaves) ? kLongSplit
+                                                                                     : kSplit;
   p.MS = decode_splits_of(a.max_blocks, a.block_size, p.split);
   const size_t slots = (size_t)a.S * a.Hq * p.MS;
   p.opart = static_cast<float*>(a.workspace);

@@ -101,14 +101,16 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
-// Tokens per key-range split of the decode kernel (512, or 1024 when the grid of 1024-token
-// ranges has at least kLongSplitMinWaves waves: eight rounds of the 1280 waves the chip holds at
-// once, five 32 KB rings per CU), key ranges per sequence in its grid, and the resulting
-// workspace size.  decode_splits counts 512-token ranges, the larger count, so the workspace and
-// the grid-size check hold for either length.
+// Tokens per key-range split of the decode kernel (512, or 1024 when the block table holds at
+// least kLongSplitMinRanges such ranges and the grid of 1024-token ranges has at least
+// kLongSplitMinWaves waves: four rounds of the 1280 waves the chip holds at once, five 32 KB
+// rings per CU), key ranges per sequence in its grid, and the resulting workspace size.
+// decode_splits counts 512-token ranges, the larger count, so the workspace and the grid-size
+// check hold for either length.
 constexpr int kDecodeSplitTokens = 512;
 constexpr int kDecodeLongSplitTokens = 1024;
-constexpr long long kLongSplitMinWaves = 8LL * 5 * 256;
+constexpr int kLongSplitMinRanges = 8;
+constexpr long long kLongSplitMinWaves = 4LL * 5 * 256;
 int decode_splits(int max_blocks, int block_size);
 int decode_splits_of(int max_blocks, int block_size, int split);
 size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size);

@@ -111,7 +111,8 @@ def test_decode_range_counts_around_the_xcd_padding(max_blocks):
     # 255 blocks = 8 ranges of 512 tokens (raised to 15 per sequence), 256 = 8 (15), 512 = 16
     # (23): sequences of every length up to the table's capacity, empty ones included.  With 40
     # sequences and 4 kv heads the grid is too small for 1024-token ranges (at most 40 * 4 * 8 =
-    # 1280 waves), so this covers the 512-token path; the 1024-token one is tested below.
+    # 1280 waves, under four rounds of 1280), so this covers the 512-token path; the 1024-token
+    # one is tested below.
     S = 40
     lens = [0] + [int(x) for x in np.linspace(1, max_blocks * 16, S - 1)]
     say(f"fa_paged_decode {S} seqs, block table of {max_blocks} blocks, lens 0..{max_blocks * 16}")
@@ -126,8 +127,9 @@ def test_decode_range_counts_around_the_xcd_padding(max_blocks):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_1024_token_ranges_ragged(d):
-    # A block table 2048 blocks wide for 64 sequences and 8 kv heads puts 64 * 8 * 32 = 16384
-    # waves in a grid of 1024-token ranges, enough for the launch to take that range length; the
+    # A block table 2048 blocks wide (32768 tokens) for 64 sequences and 8 kv heads puts
+    # 64 * 8 * 32 = 16384 waves in a grid of 1024-token ranges, so the launch takes that range
+    # length (it needs a table of more than 7168 tokens and 5120 waves); the
     # lengths sit around its edges (and the 512-token ones), with one empty sequence and one at
     # the table's capacity.  The other sequences stay short so that the cache stays small.
     S = 64
