@@ -65,9 +65,92 @@ def _time_calls(torch, fn, iters, warmup=3):
     return sum(a.elapsed_time(b) for a, b in evs) / iters
 
 
-def cpu_baseline(prefill_inputs, w, budget_s=10.0):
+class ClockSampler:
+    """Samples the GPU's engine (gfx) clock with amdsmi from a background thread while the
+    timed region runs (the main thread waits in a device synchronisation meanwhile).  The
+    published peaks assume the maximum clock; the clock held under load is recorded beside the
+    throughput.  Reports None with the reason if amdsmi cannot read the device."""
+
+    def __init__(self, torch, period_s=0.002):
+        import threading
+        self.samples, self.error, self.max_mhz = [], None, None
+        self._stop = threading.Event()
+        self._period = period_s
+        self._handle = None
+        try:
+            import amdsmi
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) == 1:
+                self._handle = handles[0]
+            else:  # match the torch device by PCI bus
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                for h in handles:
+                    if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                        self._handle = h
+            if self._handle is None:
+                raise RuntimeError(f"cannot tell which of {len(handles)} devices is cuda:0")
+            info = amdsmi.amdsmi_get_clock_info(self._handle, amdsmi.AmdSmiClkType.GFX)
+            self.max_mhz = info.get("max_clk")
+        except Exception as e:  # noqa: BLE001 -- reported in the JSON, never fatal
+            self.error = f"{type(e).__name__}: {e}"
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        per_xcd = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float))]
+        if per_xcd:
+            return sum(per_xcd) / len(per_xcd)
+        cur = m.get("current_gfxclk")
+        return cur if isinstance(cur, (int, float)) else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(float(v))
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            time.sleep(self._period)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+        return False
+
+    def report(self):
+        if not self.samples:
+            return {"mhz_median": None, "samples": 0,
+                    "note": self.error or "no clock sample during the timed region"}
+        s = sorted(self.samples)
+        return {"mhz_median": round(s[len(s) // 2], 1), "mhz_min": round(s[0], 1),
+                "mhz_max": round(s[-1], 1), "samples": len(s), "max_engine_mhz": self.max_mhz,
+                "source": "amdsmi gpu metrics (current gfx clock, mean over XCDs) during the "
+                          "timed steps"}
+
+
+def _err(got, ref):
+    import numpy as np
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref))) if ref.size else 0.0
+
+
+def cpu_baseline(prefill_inputs, w, gpu, budget_s=10.0):
     """The fp64 oracle on a bounded sample of the forward workload: successive blocks of R query
-    rows (head 0 first) against all N keys, until about budget_s seconds of CPU work."""
+    rows (head 0 first) against all N keys, until about budget_s seconds of CPU work.
+
+    ``gpu`` holds host copies of the outputs the timed GPU calls produced (the forward's o and
+    lse, the small workloads', the decode's); every oracle result computed here is also compared
+    with them, so the returned ``parity`` reports the max-abs error of each workload on exactly
+    the rows the baseline timed.  Returns (baseline, parity)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -80,12 +163,15 @@ def cpu_baseline(prefill_inputs, w, budget_s=10.0):
     R = 2048
     N, d = w["N"], w["d"]
     done, elapsed = 0, 0.0
+    eo = el = 0.0
     for h in range(w["H"]):
         for r0 in range(0, N, R):
             t0 = time.perf_counter()
-            attention_ref(qf[:, h:h + 1], kf[:, h:h + 1], vf[:, h:h + 1], 1 / math.sqrt(d),
-                          rows=list(range(r0, r0 + R)))
+            ro, rl = attention_ref(qf[:, h:h + 1], kf[:, h:h + 1], vf[:, h:h + 1], 1 / math.sqrt(d),
+                                   rows=list(range(r0, r0 + R)))
             elapsed += time.perf_counter() - t0
+            eo = max(eo, _err(gpu["fwd"][0][:, h:h + 1, r0:r0 + R], ro))
+            el = max(el, _err(gpu["fwd"][1][:, h:h + 1, r0:r0 + R], rl))
             done += 1
             if elapsed >= budget_s:
                 break
@@ -93,6 +179,11 @@ def cpu_baseline(prefill_inputs, w, budget_s=10.0):
             break
     flops = 4.0 * done * R * N * d
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    small, small_parity = oracle_small_workloads(prefill_inputs, gpu)
+    parity = {"prefill_16k": {"rows": done * R, "o_max_abs": eo, "lse_max_abs": el,
+                              "tol_o": 2e-2, "tol_lse": 1e-3}}
+    parity.update(small_parity)
+    parity["paged_decode"] = decode_parity(gpu["decode"])
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
@@ -101,14 +192,34 @@ def cpu_baseline(prefill_inputs, w, budget_s=10.0):
         "sample": f"fp64 three-pass oracle on {done} blocks of {R} query rows (head-major, "
                   f"head 0 first) x {N} keys, d={d}, {elapsed:.1f} s; flops counted as 4*rows*N*d "
                   f"like the GPU figure",
-        "small_workloads": oracle_small_workloads(prefill_inputs),
-    }
+        "small_workloads": small,
+    }, parity
 
 
-def oracle_small_workloads(prefill_inputs, repeats=3):
+def decode_parity(dec, every=4):
+    """Oracle of every `every`-th sequence of the decode workload against the GPU's output."""
+    import numpy as np
+
+    from oracle import paged_decode_ref
+
+    dq, kc, vc, table, lens, o, lse = dec
+    kcf, vcf = kc.float().numpy(), vc.float().numpy()
+    eo = el = 0.0
+    seqs = list(range(0, dq.shape[0], every))
+    for b in seqs:
+        ro, rl = paged_decode_ref(dq[b:b + 1].float().numpy().astype(np.float64), kcf, vcf,
+                                  table[b:b + 1].numpy(), [int(lens[b])], 1 / math.sqrt(dq.shape[2]))
+        eo = max(eo, _err(o[b:b + 1], ro))
+        el = max(el, _err(lse[b:b + 1], rl))
+    return {"sequences": len(seqs), "o_max_abs": eo, "lse_max_abs": el, "tol_o": 2e-2,
+            "tol_lse": 1e-3}
+
+
+def oracle_small_workloads(prefill_inputs, gpu, repeats=3):
     """The fp64 oracle over the two small workloads in full (single-head fp32 N=256 d=64, and
     B=1 H=8 N=4096 d=128), on one thread and on all host cores: median wall seconds of
-    `repeats` runs, input generation excluded."""
+    `repeats` runs, input generation excluded.  Also returns the max-abs error of the GPU's
+    outputs for them (every row)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -117,6 +228,7 @@ def oracle_small_workloads(prefill_inputs, repeats=3):
 
     all_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     res = {"cpu": _cpu_model(), "all_threads": int(all_threads)}
+    parity = {}
     for name in ("single_head_fp32", "prefill_4k"):
         w = WORKLOADS[name]
         q, k, v, _ = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], w["dtype"],
@@ -127,10 +239,14 @@ def oracle_small_workloads(prefill_inputs, repeats=3):
             with threadpool_limits(limits=limit):
                 for _ in range(repeats):
                     t0 = time.perf_counter()
-                    attention_ref(qf, kf, vf, 1 / math.sqrt(w["d"]))
+                    ro, rl = attention_ref(qf, kf, vf, 1 / math.sqrt(w["d"]))
                     times.append(time.perf_counter() - t0)
             res[f"{name}_{label}_s"] = round(sorted(times)[len(times) // 2], 4)
-    return res
+        go, gl = gpu[name]
+        parity[name] = {"rows": int(ro.shape[2]), "o_max_abs": _err(go, ro),
+                        "lse_max_abs": _err(gl, rl),
+                        "tol_o": 1e-5 if w["dtype"] == "f32" else 2e-2, "tol_lse": 1e-3}
+    return res, parity
 
 
 def _cpu_model():
@@ -292,16 +408,17 @@ def main():
     K = args.steps
     ev = [(_events(torch), _events(torch)) for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for (pa, pb), (da, db) in ev:
-        pa.record()
-        prefill()
-        pb.record()
-        da.record()
-        decode()
-        db.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler(torch) as clock:
+        t0 = time.perf_counter()
+        for (pa, pb), (da, db) in ev:
+            pa.record()
+            prefill()
+            pb.record()
+            da.record()
+            decode()
+            db.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     t_pre = sum(a.elapsed_time(b) for (a, b), _ in ev) / K      # ms
     t_dec = sum(a.elapsed_time(b) for _, (a, b) in ev) / K      # ms
 
@@ -345,6 +462,7 @@ def main():
             "ms_per_launch": round(t_pre, 4),
             "flops_per_launch": flops,
         },
+        "engine_clock": clock.report(),
         "decode": {
             "value": round(gbps, 1),
             "unit": "GB/s",
@@ -382,6 +500,25 @@ def main():
         f = acc.attention_flops(w4["B"], w4["H"], w4["N"], w4["d"], causal=True, seq_lens=lh)
         extras["gqa_varlen_8k_causal"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
                                           "seq_lens": lh}
+        # Decode on the literal reading of its pool: 4096 physical blocks (256 MiB of K and V)
+        # whose ids every sequence draws with replacement.  The pool fits the caches, so reads
+        # are mostly cache hits: reported apart, never against the HBM peak.
+        sq, skc, svc, stb, ssl = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
+                                                     wd["block_size"], wd["len_lo"], wd["len_hi"],
+                                                     seed=wd["seed"], pool_blocks=4096)
+        sbytes = acc.decode_bytes(ssl.tolist(), wd["Hq"], wd["Hkv"], wd["d"], wd["block_size"])
+        sq, skc, svc, stb, ssl = (t.to(dev) for t in (sq, skc, svc, stb, ssl))
+        so_, sl_ = torch.empty_like(sq), torch.empty((wd["S"], wd["Hq"]), dtype=torch.float32,
+                                                     device=dev)
+        t = _time_calls(torch, lambda: fa_paged_decode(sq, skc, svc, stb, ssl, so_, sl_,
+                                                       workspace=ws), 20, warmup=5)
+        extras["decode_shared_pool_4096"] = {
+            "ms": round(t, 4), "GB/s": round(sbytes / t / 1e6, 1), "bytes_per_call": sbytes,
+            "cache_resident": True,
+            "note": "block ids drawn with replacement from a 4096-block pool (256 MiB of K+V); "
+                    "the bytes are the same algorithmic count as the decode line, mostly served "
+                    "from L2/MALL, so this is not an HBM figure"}
+        del skc, svc
         # The standard unfused forward (S and P through device memory) on the 4K and 16K
         # inputs: the baseline the pages compare fused attention against.
         from io_aware_attention_02_amd import fa_fwd_unfused, fa_fwd_unfused_workspace_bytes
@@ -442,7 +579,17 @@ def main():
         out["extras"] = extras
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(prefill_inputs, wf)
+        # Host copies of what the GPU computed, for the parity report of the baseline leg.
+        gpu = {"fwd": (o.float().cpu().numpy(), lse.cpu().numpy()),
+               "decode": (dq.cpu(), kc.cpu(), vc.cpu(), table.cpu(), lens_host,
+                          do.float().cpu().numpy(), dlse.cpu().numpy())}
+        for name in ("single_head_fp32", "prefill_4k"):
+            ws_ = WORKLOADS[name]
+            qs, ks, vs, _ = prefill_inputs(ws_["B"], ws_["H"], ws_["Hkv"], ws_["N"], ws_["d"],
+                                           ws_["dtype"], seed=ws_["seed"])
+            os_, ls_ = fa_fwd(qs.to(dev), ks.to(dev), vs.to(dev))
+            gpu[name] = (os_.float().cpu().numpy(), ls_.cpu().numpy())
+        out["cpu_baseline"], out["parity"] = cpu_baseline(prefill_inputs, wf, gpu)
     else:
         out["cpu_baseline"] = None
 

@@ -25,10 +25,13 @@
  *   - Errors are reported through the return value only.  Argument validation happens before
  *     any HIP call, so an invalid call has no side effect on the device.
  *   - Values that live in device memory (sequence lengths, block ids) cannot be checked
- *     without a synchronisation: sequence lengths are clamped to their valid range inside the
- *     kernels; an out-of-range block id is undefined behaviour.
+ *     without a synchronisation, so the kernels make them safe instead: sequence lengths are
+ *     clamped to their valid range, and a block id outside [0, num_blocks) is never
+ *     dereferenced -- that block's keys and values read as zeros.
  *   - All tensors are dense, row-major, with no padding between rows.  Data pointers must be
  *     16-byte aligned.
+ *   - Sequence lengths (N, max_q, max_blocks_per_seq * block_size) above 2^30 - 1, and sizes
+ *     whose grid of workgroups would not fit a 32-bit count, return FA_ERR_UNSUPPORTED.
  */
 #ifndef FA_H
 #define FA_H
@@ -179,7 +182,9 @@ size_t fa_paged_decode_workspace_bytes(int num_seqs, int Hq, int d, int max_bloc
  *   k_cache      [num_blocks, block_size, Hkv, d] bf16
  *   v_cache      [num_blocks, block_size, Hkv, d] bf16
  *   block_table  [num_seqs, max_blocks_per_seq] int32 physical block ids in [0, num_blocks);
- *                entries at index >= ceil(L_b / block_size) are never read.
+ *                entries at index >= ceil(L_b / block_size) are never read.  Ids may repeat
+ *                (sequences sharing blocks of one pool).  An id outside [0, num_blocks) is not
+ *                an error the call can report: its block reads as zeros (keys and values 0).
  *   seq_lens     [num_seqs] int32 (device), clamped to [0, max_blocks_per_seq * block_size].
  *                A sequence of length 0 gives O = 0 and lse = -inf.
  *   o            [num_seqs, Hq, d] bf16, written.

@@ -5,7 +5,7 @@
 // stream and reports the launch status.  Nothing here allocates, synchronises or prints.
 #include "fa.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <climits>
 #include <cmath>
@@ -18,6 +18,14 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_scale(float s) { return std::isfinite(s) && s >= 0.f; }
+
+// Sequence positions (and position + tile size) stay in 32-bit integers inside the kernels.
+constexpr int kMaxN = INT_MAX / 2;
+
+// a * b * c <= limit for positive factors, decided without overflowing.
+bool product_at_most(long long limit, long long a, long long b, long long c) {
+  return a <= limit / b && a * b <= limit / c;
+}
 
 }  // namespace
 
@@ -50,8 +58,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // One workgroup per (batch, head, query tile of >= 32 rows) must fit a 1-D grid.
-  const long long tiles = (long long)B * H * ((N + 31) / 32);
-  if (tiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+  if (N > kMaxN || !product_at_most(INT_MAX, B, H, (N + 31) / 32)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdArgs a;
   a.q = q;
@@ -85,8 +92,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale,
       (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const long long tiles = (long long)B * H * ((N + 127) / 128);
-  if (tiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+  if (N > kMaxN || !product_at_most(INT_MAX, B, H, (N + 127) / 128)) return FA_ERR_UNSUPPORTED;
   fa::Fp8FwdArgs a;
   a.q = q;
   a.k = k;
@@ -124,9 +130,10 @@ fa_status fa_fwd_unfused(const void* q, const void* k, const void* v, void* o, f
     return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (N % 8 != 0) return FA_ERR_UNSUPPORTED;  // aligned 16-byte score and 8-byte P accesses
-  const long long tiles = (long long)B * H * ((N + 127) / 128);
-  const long long rows = (long long)B * H * N;
-  if (tiles > INT_MAX || rows / 4 + 1 > INT_MAX) return FA_ERR_UNSUPPORTED;
+  // Grids: one workgroup per (batch, head, 128 rows), and one per 4 rows of the softmax pass.
+  if (N > kMaxN || !product_at_most(INT_MAX, B, H, (N + 127) / 128) ||
+      !product_at_most(4LL * (INT_MAX - 1), B, H, N))
+    return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa::unfused_workspace_bytes(B, H, N)) return FA_ERR_INVALID_ARG;
   fa::UnfusedArgs a;
   a.q = q;
@@ -167,8 +174,8 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
   if (block_size != 16) return FA_ERR_UNSUPPORTED;
   // One workgroup per (sequence, query head, tile of >= 128 query rows); key positions and
   // offsets in 32-bit integers.
-  const long long tiles = (long long)num_seqs * Hq * ((max_q + 127) / 128);
-  if (tiles > INT_MAX || (long long)max_blocks_per_seq * block_size > INT_MAX / 2)
+  if (max_q > kMaxN || !product_at_most(INT_MAX, num_seqs, Hq, (max_q + 127) / 128) ||
+      (long long)max_blocks_per_seq * block_size > kMaxN)
     return FA_ERR_UNSUPPORTED;
 
   fa::PagedPrefillArgs a;
@@ -186,6 +193,7 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
   a.Hkv = Hkv;
   a.d = d;
   a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
   a.scale = scale;
   const hipError_t e = fa::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -209,9 +217,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;  // unknown, or fp32 (forward only)
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // Grids: one workgroup per (batch, head, 128 rows), and one per 16 rows of the row pass.
-  const long long tiles = (long long)B * H * ((N + 127) / 128);
-  const long long rows = (long long)B * H * N;
-  if (tiles > INT_MAX || rows / 16 + 1 > INT_MAX) return FA_ERR_UNSUPPORTED;
+  if (N > kMaxN || !product_at_most(INT_MAX, B, H, (N + 127) / 128) ||
+      !product_at_most(16LL * (INT_MAX - 1), B, H, N))
+    return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa::bwd_workspace_bytes(B, H, N)) return FA_ERR_INVALID_ARG;
 
   fa::BwdArgs a;
@@ -263,10 +271,10 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
   if (Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
   // Grid: one 64-thread workgroup per (kv head, key range, sequence), at most one per 512 tokens, rounded up
   // to a multiple of 8 ranges; the total thread count must fit a 32-bit grid.
-  if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return FA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_UNSUPPORTED;
   const long long splits = fa::decode_splits(max_blocks_per_seq, block_size);
   const long long units = ((long long)num_seqs * splits + 7) / 8 * 8;
-  if (units * Hkv * 64 > INT_MAX) return FA_ERR_UNSUPPORTED;
+  if (!product_at_most(INT_MAX, units, Hkv, 64)) return FA_ERR_UNSUPPORTED;
   const size_t need =
       fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);
   if (workspace_bytes < need) return FA_ERR_INVALID_ARG;

@@ -548,10 +548,6 @@ bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-// Floats in one per-row statistics array (D or the base-2 LSE) of the workspace, rounded up to
-// 256 bytes.
-size_t stat_floats(int B, int H, int N) { return ((size_t)B * H * N + 63) / 64 * 64; }
-
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   BwdParams p;
@@ -565,7 +561,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   p.dk = static_cast<bf16*>(a.dk);
   p.dv = static_cast<bf16*>(a.dv);
   p.dvec = static_cast<float*>(a.workspace);
-  p.lse2 = p.dvec + stat_floats(a.B, a.H, a.N);
+  p.lse2 = p.dvec + bwd_stat_floats(a.B, a.H, a.N);
   p.seq_lens = a.seq_lens;
   p.B = a.B;
   p.H = a.H;
@@ -587,11 +583,6 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-size_t bwd_workspace_bytes(int B, int H, int N) {
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return 2 * stat_floats(B, H, N) * sizeof(float);
-}
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);

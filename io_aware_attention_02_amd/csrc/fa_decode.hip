@@ -64,6 +64,7 @@ struct DecodeParams {
   float* mpart;  // [S][Hq][MS]
   float* lpart;  // [S][Hq][MS]
   int Hq, Hkv, group, max_blocks, max_tokens, MS, units;
+  int num_blocks;  // blocks in the pool: ids outside [0, num_blocks) are never dereferenced
   int split;  // tokens per key range: kSplit or kLongSplit
   float sl2;
 };
@@ -201,9 +202,16 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeParams p) {
                 : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
-  auto res_of = [&](int i) __attribute__((always_inline)) {  // scalar resources of block i of the range (empty past the end)
-    const int bid = __builtin_amdgcn_readlane(my_bid, min(i, n_blk - 1));
-    const int valid = i < n_blk ? min(kBS, tok_end - (tok_begin + i * kBS)) : 0;
+  // Scalar resources of block i of the range: empty past the end of the range, and empty for a
+  // block id outside the pool (its keys and values then read as zeros; nothing outside the pool
+  // is addressed).
+  auto res_of = [&](int i) __attribute__((always_inline)) {
+    int bid = __builtin_amdgcn_readlane(my_bid, min(i, n_blk - 1));
+    int valid = i < n_blk ? min(kBS, tok_end - (tok_begin + i * kBS)) : 0;
+    if ((unsigned)bid >= (unsigned)p.num_blocks) {
+      bid = 0;
+      valid = 0;
+    }
     return block_res<D>(p, bid, valid, row_bytes);
   };
 
@@ -378,6 +386,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.group = a.Hq / a.Hkv;
   p.max_blocks = a.max_blocks;
   p.max_tokens = a.max_blocks * a.block_size;
+  p.num_blocks = a.num_blocks;
   // Range length: 1024 tokens when a full-length sequence still has at least 8 ranges and the
   // grid at least four rounds of waves (fewer partial results, and each wave's load ramp is paid
   // over twice the tokens), else 512: short contexts cut into 1024-token ranges leave a ragged
@@ -404,32 +413,6 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-// Key ranges per sequence in the split grid (the workspace holds one partial result per range):
-// ceil(max tokens / range length), raised to 7 mod 8 once there are at least 8.  Work unit u = b * MS + sp
-// runs on XCD u mod 8 (workgroups are dealt round-robin over the XCDs), so with MS = 7 mod 8,
-// range sp of sequence b lands on XCD (sp - b) mod 8: each sequence starts on a different XCD,
-// and the ranges left over after whole rounds of 8 (and the empty ones past a short sequence's
-// end) spread over all XCDs instead of piling onto the low-numbered ones.  The added ranges are
-// empty and exit at once.
-int decode_splits_of(int max_blocks, int block_size, int split) {
-  const long long tokens = (long long)max_blocks * block_size;
-  int ms = (int)((tokens + split - 1) / split);
-  if (ms >= kXcds) ms += kXcds - 1 - ms % kXcds;
-  return ms;
-}
-
-// The 512-token count bounds the 1024-token one (both steps are monotone in the token count), so
-// the workspace and the grid-size check use it whichever length the launch picks.
-int decode_splits(int max_blocks, int block_size) {
-  return decode_splits_of(max_blocks, block_size, kSplit);
-}
-
-size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size) {
-  if (S <= 0 || Hq <= 0 || d <= 0 || max_blocks <= 0 || block_size <= 0) return 0;
-  const size_t slots = (size_t)S * Hq * decode_splits(max_blocks, block_size);
-  return slots * ((size_t)d + 2) * sizeof(float);
-}
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   return a.d == 128 ? launch<128>(a, stream) : launch<64>(a, stream);

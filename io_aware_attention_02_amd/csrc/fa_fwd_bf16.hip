@@ -64,6 +64,7 @@ struct Params {
   const int32_t* table;     // paged: block table [B, max_blocks]
   const int32_t* q_lens;    // paged: query rows per sequence (its newest tokens)
   int H, group, Hkv, N, n_qt, total, max_blocks;
+  int num_blocks;  // paged: blocks in the pool; ids outside [0, num_blocks) are never dereferenced
   float sl2;  // scale * log2(e): scores go to the exponent base 2
 };
 
@@ -319,7 +320,10 @@ fwd_bf16_kernel(Params p) {
   int bid_next = 0;
   auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt, int bid) __attribute__((always_inline)) {
     if constexpr (PAGED) {
-      const int valid = min(max(L - (jt * kBN + wblk * kPageRows), 0), kPageRows);
+      // A block id outside the pool gets an empty resource: its rows read as zeros.
+      const bool in_pool = (unsigned)bid < (unsigned)p.num_blocks;
+      const int valid = in_pool ? min(max(L - (jt * kBN + wblk * kPageRows), 0), kPageRows) : 0;
+      bid = in_pool ? bid : 0;
       load_tile_paged<D, NW>(Kd, p.k, bid, g, valid, p.Hkv, koff, wave);
       load_tile_paged<D, NW>(Vd, p.v, bid, g, valid, p.Hkv, voff, wave);
     } else {
@@ -538,6 +542,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.table = nullptr;
   p.q_lens = nullptr;
   p.max_blocks = 0;
+  p.num_blocks = 0;
   p.H = a.H;
   p.group = a.H / a.Hkv;
   p.Hkv = a.Hkv;
@@ -581,6 +586,7 @@ hipError_t launch_paged(const PagedPrefillArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.N = a.max_q;
   p.max_blocks = a.max_blocks;
+  p.num_blocks = a.num_blocks;
   p.sl2 = a.scale * kLog2e;
   // Four waves (128 query rows) per workgroup, two workgroups per CU: chunks are often much
   // shorter than 256 rows, and a wave whose rows are all padding idles its SIMD.

@@ -2,7 +2,7 @@
 // Arguments are already validated when these run; each returns the HIP launch status.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -75,7 +75,7 @@ struct PagedPrefillArgs {
   const int32_t* q_lens;
   void* o;     // [S, Hq, max_q, d]
   float* lse;  // [S, Hq, max_q]
-  int S, max_q, Hq, Hkv, d, max_blocks;
+  int S, max_q, Hq, Hkv, d, max_blocks, num_blocks;
   float scale;
 };
 
@@ -99,6 +99,8 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int B, int H, int N);
+// Floats in one per-row statistics array (D or the base-2 LSE) of the backward's workspace.
+size_t bwd_stat_floats(int B, int H, int N);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
 // Tokens per key-range split of the decode kernel (512, or 1024 when the block table holds at

@@ -233,11 +233,6 @@ hipError_t launch(const UnfusedArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t unfused_workspace_bytes(int B, int H, int N) {
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)B * H * N * N * (sizeof(float) + sizeof(bf16));
-}
-
 hipError_t launch_fwd_unfused(const UnfusedArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
   return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);

@@ -19,6 +19,10 @@ Recipe (the workload list that the measurements quote):
   [num_blocks, block_size, Hkv, d], all N(0, 1) rounded to bf16.  Unused block-table entries
   are -1.  The pool holds exactly sum(ceil(L_b / block_size)) blocks, so every cached byte is
   distinct and comes from HBM once per decode step.
+* shared fixed pool (``pool_blocks=P``): the literal reading of a pool of P physical blocks
+  that every sequence draws from.  Instead of the permutation, each logical block's id is drawn
+  uniformly from [0, P) with replacement, so ids repeat across sequences and inside one
+  sequence; the pools then hold P blocks.  The rest of the recipe is unchanged.
 """
 
 import math
@@ -118,12 +122,37 @@ def varlen_lengths(B, lo, hi, gen):
     return torch.randint(int(lo), int(hi) + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
 
 
+def _block_table(nblk, gen, spare_blocks=0, pool_blocks=None):
+    """(block_table [S, max_blocks] int32, pool size): distinct ids placed by a random permutation
+    of sum(nblk) + spare_blocks blocks, or, with ``pool_blocks``, ids drawn uniformly with
+    replacement from [0, pool_blocks).  Unused entries are -1."""
+    S = len(nblk)
+    max_blocks = max(1, max(nblk))
+    used = sum(nblk)
+    if pool_blocks is None:
+        pool = used + int(spare_blocks)
+        ids = torch.randperm(max(pool, 1), generator=gen, dtype=torch.int64)[:pool]
+    else:
+        pool = int(pool_blocks)
+        if pool <= 0:
+            raise ValueError("pool_blocks must be positive")
+        ids = torch.randint(0, pool, (used,), generator=gen, dtype=torch.int64)
+    table = torch.full((S, max_blocks), -1, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = ids[pos:pos + n].to(torch.int32)
+        pos += n
+    return table, pool
+
+
 def paged_decode_inputs(S, Hq, Hkv, d, block_size=16, len_lo=512, len_hi=32768, seed=0,
-                        seq_lens=None, spare_blocks=0):
+                        seq_lens=None, spare_blocks=0, pool_blocks=None):
     """(q, k_cache, v_cache, block_table, seq_lens) on the CPU, bf16 data, int32 indices.
 
     ``seq_lens`` may be given explicitly (a list); otherwise it is drawn.  ``spare_blocks``
     adds unreferenced blocks to the pool (their ids are shuffled in with the used ones).
+    ``pool_blocks`` switches to a shared pool of that many blocks with ids drawn with
+    replacement (``spare_blocks`` is then ignored).
     """
     g = _gen(seed)
     if seq_lens is None:
@@ -133,15 +162,7 @@ def paged_decode_inputs(S, Hq, Hkv, d, block_size=16, len_lo=512, len_hi=32768, 
         if lens.numel() != S:
             raise ValueError("seq_lens must have S entries")
     nblk = [int(math.ceil(int(x) / block_size)) for x in lens]
-    max_blocks = max(1, max(nblk))
-    used = sum(nblk)
-    pool = used + int(spare_blocks)
-    perm = torch.randperm(max(pool, 1), generator=g, dtype=torch.int64)[:pool]
-    table = torch.full((S, max_blocks), -1, dtype=torch.int32)
-    pos = 0
-    for b, n in enumerate(nblk):
-        table[b, :n] = perm[pos:pos + n].to(torch.int32)
-        pos += n
+    table, pool = _block_table(nblk, g, spare_blocks, pool_blocks)
     q = _randn((S, Hq, d), g, torch.bfloat16)
     k_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
     v_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
@@ -149,22 +170,16 @@ def paged_decode_inputs(S, Hq, Hkv, d, block_size=16, len_lo=512, len_hi=32768, 
 
 
 def paged_prefill_inputs(S, Hq, Hkv, d, max_q, block_size=16, len_lo=512, len_hi=32768, seed=0,
-                         seq_lens=None, q_lens=None, spare_blocks=0):
-    """(q [S,Hq,max_q,d], k_cache, v_cache, block_table, seq_lens, q_lens) on the CPU."""
+                         seq_lens=None, q_lens=None, spare_blocks=0, pool_blocks=None):
+    """(q [S,Hq,max_q,d], k_cache, v_cache, block_table, seq_lens, q_lens) on the CPU.
+    ``pool_blocks`` as for ``paged_decode_inputs``."""
     g = _gen(seed)
     if seq_lens is None:
         lens = torch.randint(int(len_lo), int(len_hi) + 1, (S,), generator=g, dtype=torch.int64)
     else:
         lens = torch.as_tensor(list(seq_lens), dtype=torch.int64)
     nblk = [int(math.ceil(int(x) / block_size)) for x in lens]
-    max_blocks = max(1, max(nblk))
-    pool = sum(nblk) + int(spare_blocks)
-    perm = torch.randperm(max(pool, 1), generator=g, dtype=torch.int64)[:pool]
-    table = torch.full((S, max_blocks), -1, dtype=torch.int32)
-    pos = 0
-    for b, n in enumerate(nblk):
-        table[b, :n] = perm[pos:pos + n].to(torch.int32)
-        pos += n
+    table, pool = _block_table(nblk, g, spare_blocks, pool_blocks)
     q = _randn((S, Hq, max_q, d), g, torch.bfloat16)
     k_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)
     v_cache = _randn((max(pool, 1), block_size, Hkv, d), g, torch.bfloat16)

@@ -75,8 +75,14 @@ def paged_decode_ref(q, k_cache, v_cache, block_table, seq_lens, scale):
     return o, lse
 
 
-def paged_prefill_ref(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale):
-    """Chunked prefill: O [S, Hq, Qmax, d] and LSE [S, Hq, Qmax] in float64."""
+def paged_prefill_ref(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale, rows=None):
+    """Chunked prefill: O [S, Hq, Qmax, d] and LSE [S, Hq, Qmax] in float64.
+
+    rows: None for every query row, or a 1-D list of query-row indices (into Qmax) to compute;
+    then the results are [S, Hq, n_rows, d] and [S, Hq, n_rows] (each row's softmax involves
+    that row alone, so a subset is exact for those rows).  Rows at or past a sequence's chunk
+    length are padding: O = 0, LSE = -inf.
+    """
     q = np.asarray(q, dtype=np.float64)
     S, Hq, Qmax, d = q.shape
     Hkv = k_cache.shape[2]
@@ -85,20 +91,25 @@ def paged_prefill_ref(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale)
     group = Hq // Hkv
     lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
     qls = [int(x) for x in np.asarray(q_lens).reshape(-1)]
-    o = np.zeros((S, Hq, Qmax, d))
-    lse = np.full((S, Hq, Qmax), -np.inf)
+    sel = np.arange(Qmax) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    if sel.size and (sel.min() < 0 or sel.max() >= Qmax):
+        raise ValueError("rows out of range")
+    o = np.zeros((S, Hq, sel.size, d))
+    lse = np.full((S, Hq, sel.size), -np.inf)
     for b in range(S):
         L, Q = lens[b], qls[b]
         if Q > L or Q > Qmax:
             raise ValueError("q_lens must not exceed seq_lens or the query rows")
-        if Q == 0:
+        valid = sel < Q
+        if Q == 0 or not valid.any():
             continue
         kb = gather_paged_kv(k_cache, block_table[b], L)    # [L, Hkv, d]
         vb = gather_paged_kv(v_cache, block_table[b], L)
-        counts = (L - Q) + np.arange(Q) + 1                  # keys visible to each query row
+        counts = (L - Q) + sel[valid] + 1                    # keys visible to each query row
         for h in range(Hq):
             g = h // group
-            ob, lb, _ = _three_pass(q[b, h, :Q], kb[:, g, :], vb[:, g, :], float(scale), counts)
-            o[b, h, :Q] = ob
-            lse[b, h, :Q] = lb
+            ob, lb, _ = _three_pass(q[b, h, sel[valid]], kb[:, g, :], vb[:, g, :], float(scale),
+                                    counts)
+            o[b, h, valid] = ob
+            lse[b, h, valid] = lb
     return o, lse

@@ -35,3 +35,13 @@ def max_abs(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def tile_rows(N, tile, head, seed=0, edges=True):
+    """Query rows that reach every `tile`-row query tile: one row per tile, drawn per head (so the
+    heads of a grid see different rows), plus the tile edges 0, tile - 1, tile and N - 1."""
+    g = np.random.default_rng(1000 * seed + head)
+    rows = {min(N - 1, t + int(g.integers(0, tile))) for t in range(0, N, tile)}
+    if edges:
+        rows |= {r for r in (0, tile - 1, tile, N - 1) if 0 <= r < N}
+    return sorted(rows)

@@ -19,7 +19,7 @@ from io_aware_attention_02_amd import fa_bwd, fa_fwd
 from io_aware_attention_02_amd.inputs import WORKLOADS, output_gradient, prefill_inputs
 from oracle import attention_bwd_ref
 
-from gpu_common import device, f64, max_abs, say
+from gpu_common import device, f64, max_abs, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -141,24 +141,71 @@ def test_bwd_prefill_4k_workload():
     _check(q, k, v, do, dq, dk, dv, w["causal"], None, 1 / w["d"] ** 0.5)
 
 
+def _sampled_refs(q, k, v, do, causal, lens, scale, seed):
+    """Oracle dQ of one row per 128-row query tile and dK, dV of one key per 128-key tile, drawn
+    per head (kv head for keys), plus the tile edges and the rows around each length.  The
+    (batch, kv head) units run in a thread pool (numpy releases the interpreter lock)."""
+    import concurrent.futures
+    B, H, N = q.shape[0], q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    group = H // Hkv
+
+    def pick(b, idx):
+        r = set(tile_rows(N, 128, idx + 100 * b, seed))
+        if lens is not None:
+            r |= {x for x in (lens[b] - 2, lens[b] - 1, lens[b], lens[b] + 1) if 0 <= x < N}
+        return sorted(r)
+
+    def unit(bg):
+        b, g = bg
+        hs = slice(g * group, (g + 1) * group)
+        sl = None if lens is None else [lens[b]]
+        args = (f64(q[b:b + 1, hs]), f64(k[b:b + 1, g:g + 1]), f64(v[b:b + 1, g:g + 1]),
+                f64(do[b:b + 1, hs]))
+        rows = [pick(b, h) for h in range(g * group, (g + 1) * group)]
+        dqs = [attention_bwd_ref(args[0][:, j:j + 1], args[1], args[2], args[3][:, j:j + 1],
+                                 scale, causal=causal, seq_lens=sl, rows=rows[j])[0]
+               for j in range(group)]
+        keys = pick(b, 1000 + g)
+        _, dk, dv = attention_bwd_ref(*args, scale, causal=causal, seq_lens=sl, keys=keys)
+        return b, g, rows, dqs, keys, dk, dv
+
+    units = [(b, g) for b in range(B) for g in range(Hkv)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        return list(ex.map(unit, units))
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["prefill_16k", "prefill_16k_causal", "gqa_varlen_8k"])
-def test_bwd_large_workload_sampled_rows(name):
+def test_bwd_large_workload_sampled_rows_and_keys(name):
     w = WORKLOADS[name]
-    say(f"fa_bwd {name} sampled dQ rows")
+    say(f"fa_bwd {name}: dQ of a row per 128-row tile, dK and dV of a key per 128-key tile, "
+        "every head")
     q, k, v, lens = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], w["dtype"],
                                    seed=w["seed"], len_lo=w.get("len_lo"), len_hi=w.get("len_hi"))
     do = output_gradient(w["B"], w["H"], w["N"], w["d"], seed=w["seed"])
     dq, dk, dv = _run(q, k, v, do, w["causal"], seq_lens=lens)
+    gq, gk, gv = f64(dq), f64(dk), f64(dv)
+    for t, nm in ((gq, "dQ"), (gk, "dK"), (gv, "dV")):
+        assert np.isfinite(t).all(), f"{nm} has non-finite values"
     N = w["N"]
-    rows = [0, 1, 63, 64, 4095, N // 2 + 17, N - 2, N - 1]
     ll = None if lens is None else lens.tolist()
-    ref, _, _ = attention_bwd_ref(f64(q), f64(k), f64(v), f64(do), 1 / w["d"] ** 0.5,
-                                  causal=w["causal"], seq_lens=ll, rows=rows)
-    got = f64(dq)[:, :, rows]
-    for b in range(w["B"]):
+    res = _sampled_refs(q, k, v, do, w["causal"], ll, 1 / w["d"] ** 0.5, w["seed"])
+    group = w["H"] // w["Hkv"]
+    # Tolerance normaliser: the largest magnitude of each sampled oracle tensor, over all units.
+    nq = max(float(np.abs(r).max()) for u in res for r in u[3])
+    nk = max(float(np.abs(u[5]).max()) for u in res)
+    nv = max(float(np.abs(u[6]).max()) for u in res)
+    for b, g, rows, dqs, keys, rk, rv in res:
         L = N if ll is None else ll[b]
-        sel = np.asarray(rows) < L
-        _compare(f"dQ[{b}] sampled", got[b][:, sel], ref[b][:, sel], ref)
-        assert (got[b][:, ~sel] == 0).all()
-    for t, nm in ((dk, "dK"), (dv, "dV")):
-        assert torch.isfinite(t.float()).all(), f"{nm} has non-finite values"
+        for j, (r, ref) in enumerate(zip(rows, dqs)):
+            h = g * group + j
+            sel = np.asarray(r) < L
+            got = gq[b, h][r]
+            _compare(f"dQ[{b},{h}] sampled", got[sel], ref[0, 0][sel], np.array([nq]))
+            assert (got[~sel] == 0).all(), f"dQ[{b},{h}]: padding rows not zero"
+        sel = np.asarray(keys) < L
+        _compare(f"dK[{b},{g}] sampled", gk[b, g][keys][sel], rk[0, 0][sel], np.array([nk]))
+        _compare(f"dV[{b},{g}] sampled", gv[b, g][keys][sel], rv[0, 0][sel], np.array([nv]))
+        assert (gk[b, g][keys][~sel] == 0).all() and (gv[b, g][keys][~sel] == 0).all(), \
+            f"({b},{g}): keys past the length have nonzero dK/dV"

@@ -95,13 +95,15 @@ def test_decode_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("seed", [None, 101, 102, 103])  # the workload's own seed, then repeats
-def test_paged_decode_workload(seed):
+@pytest.mark.parametrize("seed,pool", [(None, None), (101, None), (102, None), (103, None),
+                                       (None, 4096)])  # the workload's seed, repeats, shared pool
+def test_paged_decode_workload(seed, pool):
     w = WORKLOADS["paged_decode"]
     seed = w["seed"] if seed is None else seed
-    say(f"fa_paged_decode 64 seqs Hq=32 Hkv=8 d=128 lens U[512,32768] (every sequence), seed {seed}")
+    say(f"fa_paged_decode 64 seqs Hq=32 Hkv=8 d=128 lens U[512,32768] (every sequence), seed {seed}"
+        f", pool {pool or 'distinct blocks'}")
     q, kc, vc, table, sl = paged_decode_inputs(w["S"], w["Hq"], w["Hkv"], w["d"], w["block_size"],
-                                               w["len_lo"], w["len_hi"], seed=seed)
+                                               w["len_lo"], w["len_hi"], seed=seed, pool_blocks=pool)
     o, lse = _run(q, kc, vc, table, sl)
     _check(q, kc, vc, table, sl, o, lse, 1 / 128 ** 0.5)
 
@@ -140,3 +142,36 @@ def test_decode_1024_token_ranges_ragged(d):
     assert table.shape[1] == 2048
     o, lse = _run(q, kc, vc, table, sl)
     _check(q, kc, vc, table, sl, o, lse, 1 / d ** 0.5)
+
+
+def test_decode_shared_pool_with_repeated_ids():
+    # The literal reading of the decode workload's pool: 4096 physical blocks that every
+    # sequence draws its ids from, with replacement.
+    lens = [1, 17, 500, 4097, 9000, 20000, 32768, 0]
+    say(f"fa_paged_decode 4096-block shared pool, ids drawn with replacement, lens={lens}")
+    q, kc, vc, table, sl = paged_decode_inputs(len(lens), 32, 8, 128, 16, seed=324, seq_lens=lens,
+                                               pool_blocks=4096)
+    table[2, 9] = table[2, 4]          # the same block twice in one sequence, for certain
+    o, lse = _run(q, kc, vc, table, sl)
+    _check(q, kc, vc, table, sl, o, lse, 1 / 128 ** 0.5)
+
+
+def test_decode_block_ids_outside_the_pool_read_as_zeros():
+    # An id outside [0, num_blocks) is never dereferenced: that block's keys and values read as
+    # zeros.  The oracle sees the same table with those ids pointing at an all-zero block.
+    lens = [700, 33, 1600]
+    q, kc, vc, table, sl = paged_decode_inputs(3, 16, 4, 128, 16, seed=325, seq_lens=lens,
+                                               spare_blocks=2)
+    P = kc.shape[0]
+    bad = table.clone()
+    bad[0, 5] = P
+    bad[1, 1] = -1
+    bad[2, 99] = 1 << 30
+    o, lse = _run(q, kc, vc, bad, sl)
+    kz = torch.cat([kc, torch.zeros_like(kc[:1])])
+    vz = torch.cat([vc, torch.zeros_like(vc[:1])])
+    ref_table = table.clone()
+    ref_table[0, 5] = P
+    ref_table[1, 1] = P
+    ref_table[2, 99] = P
+    _check(q, kz, vz, ref_table, sl, o, lse, 1 / 128 ** 0.5)

@@ -1,21 +1,19 @@
-"""GPU parity of fa_fwd_fp8 (through the C ABI) against the fp64 FP8 oracle.
+"""GPU parity of fa_fwd_fp8 (through the C ABI) against the fp64 oracle.
 
-Inputs are the N(0,1) prefill tensors quantised per tensor to e4m3 (descale amax / 448).  Two
-comparisons:
+The oracle is the plain definition: the exact attention, in float64, of the tensors the e4m3
+codes stand for (codes decoded and multiplied by their descale factors).  The kernel rounds the
+probabilities to e4m3 before the P V product, so its outputs differ from that definition by
+rounding errors whose size the e4m3 format fixes; ``tests/fp8_bounds.py`` derives the
+tolerance (elementwise, and the mean squared error of each tensor against its variance bound)
+and ``tests/test_fp8_tolerance.py`` shows on the CPU that it admits correct rounding schemes
+and rejects plausible mistakes.  The LSE uses unrounded probabilities and is compared with the
+LSE tolerance.
 
-* against ``attention_fp8_ref`` with the kernel's softmax block (64 keys): the same arithmetic
-  in fp64.  What separates the two:
-    - the bf16 rounding of the output: at most 2^-8 |O| (half a bf16 unit, relative);
-    - the scores: the FP8 MFMA accumulates its 64-deep products with ~1e-3 relative error
-      (measured against exact dot products), which moves a probability by ~1e-4 relative;
-      that is harmless in itself, but a probability whose 256 p lies that close to an e4m3
-      rounding midpoint rounds the other way: one e4m3 step, at most 2^-3 of that p.
-  Bound per element: 2^-8 |O_ref| + 2^-3 * FLIPS * pmax_i * max|V| + 1e-4, with pmax_i the
-  row's largest probability exp(max_j S_ij - LSE_i) and FLIPS = 2 flipped keys per row.
-* against the exact attention of the dequantised inputs (small shapes): every rounded
-  probability is within one e4m3 step of the exact one, so |O - O_exact| <= 2^-3 sum_j P_ij |V_j|
-  + 2^-16 sum_j |V_j| (subnormal floor: half of 2^-9 / 64) + the bf16 rounding.
-LSE: the row sums use unrounded probabilities, so the LSE is compared with TOL_LSE.
+Inputs are the N(0,1) prefill tensors quantised per tensor to e4m3 (descale amax / 448).
+Shapes cover ragged lengths, both masks, grouped heads and d = 64 / 128; padding lengths with
+the e4m3 NaN code in every padded row; scale 0; the 4K workload in full; the 16K workloads on
+one sampled row of every 128-row query tile of every head (rows drawn per head) plus the tile
+edges.
 """
 
 import numpy as np
@@ -24,14 +22,12 @@ import torch
 
 from io_aware_attention_02_amd import fa_fwd_fp8
 from io_aware_attention_02_amd.inputs import WORKLOADS, fp8_inputs
-from oracle import attention_fp8_ref, attention_probs_ref, e4m3_decode
+from oracle import attention_probs_ref, e4m3_decode
 
-from gpu_common import TOL_LSE, device, f64, max_abs, say
+from fp8_bounds import check_against_exact
+from gpu_common import TOL_LSE, device, f64, max_abs, say, tile_rows
 
 pytestmark = pytest.mark.gpu
-
-BLOCK = 64
-FLIPS = 2
 
 
 def _run(q8, k8, v8, scales, causal, seq_lens=None, scale=None):
@@ -43,70 +39,43 @@ def _run(q8, k8, v8, scales, causal, seq_lens=None, scale=None):
     return f64(o), f64(lse)
 
 
-def _row_pmax(q8, k8, scales, causal, lens, scale, lse_ref, rows):
-    """Largest probability of each row, exp(max_j S_ij - LSE_i), from the oracle's LSE."""
-    qs, ks, _ = scales
-    q = e4m3_decode(q8.numpy()) * qs
-    k = e4m3_decode(k8.numpy()) * ks
-    B, H, N = q.shape[0], q.shape[1], q.shape[2]
-    group = H // k.shape[1]
-    out = np.zeros((B, H, len(rows)))
-    for b in range(B):
-        L = N if lens is None else lens[b]
-        for h in range(H):
-            for t, i in enumerate(rows):
-                if i >= L:
-                    continue
-                cnt = min(i + 1, L) if causal else L
-                s = scale * (k[b, h // group, :cnt] @ q[b, h, i])
-                out[b, h, t] = np.exp(s.max() - lse_ref[b, h, t])
-    return out
+def _dequantised(q8, k8, v8, scales):
+    qs, ks, vs = scales
+    return (e4m3_decode(q8.numpy()) * qs, e4m3_decode(k8.numpy()) * ks,
+            e4m3_decode(v8.numpy()) * vs)
 
 
-def _check_vs_oracle(q8, k8, v8, scales, causal, lens, scale, go, gl, rows=None):
-    ro, rl = attention_fp8_ref(q8.numpy(), k8.numpy(), v8.numpy(), *scales, scale, causal=causal,
-                               seq_lens=lens, block=BLOCK, rows=rows)
-    N = q8.shape[2]
+def _check(q8, k8, v8, scales, causal, lens, scale, go, gl, rows=None):
+    """Exact-attention parity of the rows ``rows`` (all rows if None) of every (batch, head)."""
+    q, k, v = _dequantised(q8, k8, v8, scales)
+    ro, rl, p = attention_probs_ref(q, k, v, scale, causal=causal, seq_lens=lens, rows=rows)
+    group = q.shape[1] // k.shape[1]
+    worst, agg = check_against_exact(go, ro, p, v, group, lens=lens, rows=rows)
+    assert agg <= 1.0, f"mean squared error {agg:.3f} x its e4m3 variance bound"
+    N = q.shape[2]
     sel = np.arange(N) if rows is None else np.asarray(rows)
-    pmax = _row_pmax(q8, k8, scales, causal, lens, scale, rl, sel)
-    vmax = float(np.abs(e4m3_decode(v8.numpy())).max()) * scales[2]
-    worst = 0.0
-    for b in range(q8.shape[0]):
+    for b in range(q.shape[0]):
         L = N if lens is None else lens[b]
         ok = sel < L
         if ok.any():
-            err = np.abs(go[b][:, ok] - ro[b][:, ok])
-            bound = (2.0 ** -8 * np.abs(ro[b][:, ok])
-                     + 2.0 ** -3 * FLIPS * pmax[b][:, ok, None] * vmax + 1e-4)
-            worst = max(worst, float(np.max(err / bound)))
-            assert (err <= bound).all(), f"batch {b}: O error {err.max():.3e} above the bound"
             el = max_abs(gl[b][:, ok], rl[b][:, ok])
             assert el <= TOL_LSE, f"batch {b}: LSE max-abs {el:.3e}"
         if (~ok).any():
             assert (go[b][:, ~ok] == 0).all(), f"batch {b}: padding rows of O not zero"
             assert np.isneginf(gl[b][:, ~ok]).all(), f"batch {b}: padding LSE not -inf"
-    say(f"  vs FP8 oracle: worst error / bound = {worst:.3f}")
+    say(f"  vs exact attention: worst error / e4m3 bound {worst:.3f}, "
+        f"mean squared error / variance bound {agg:.3f}")
 
 
-def _check_vs_exact(q8, k8, v8, scales, causal, lens, scale, go):
-    qs, ks, vs = scales
-    q, k, v = e4m3_decode(q8.numpy()) * qs, e4m3_decode(k8.numpy()) * ks, e4m3_decode(v8.numpy()) * vs
-    ro, _, p = attention_probs_ref(q, k, v, scale, causal=causal, seq_lens=lens)
-    group = q.shape[1] // k.shape[1]
-    N = q.shape[2]
-    worst = 0.0
-    for b in range(q.shape[0]):
-        L = N if lens is None else lens[b]
-        if L == 0:
-            continue
-        for h in range(q.shape[1]):
-            va = np.abs(v[b, h // group, :L])
-            bound = (2.0 ** -3 * (p[b, h, :L, :L] @ va) + 2.0 ** -16 * va.sum(axis=0)
-                     + 2.0 ** -8 * np.abs(ro[b, h, :L]) + 1e-6)
-            err = np.abs(go[b, h, :L] - ro[b, h, :L])
-            worst = max(worst, float(np.max(err / bound)))
-            assert (err <= bound).all(), f"({b},{h}): error above the e4m3 bound"
-    say(f"  vs exact attention: worst error / e4m3 bound = {worst:.3f}")
+def _check_sampled(q8, k8, v8, scales, causal, scale, go, gl, tile, seed):
+    """One row of every `tile`-row query tile of every head, drawn per head."""
+    H, Hkv = q8.shape[1], k8.shape[1]
+    group = H // Hkv
+    for h in range(H):
+        rows = tile_rows(q8.shape[2], tile, h, seed)
+        g = h // group
+        _check(q8[:, h:h + 1], k8[:, g:g + 1], v8[:, g:g + 1], scales, causal, None, scale,
+               go[:, h:h + 1, rows], gl[:, h:h + 1, rows], rows=rows)
 
 
 SHAPES = [
@@ -129,10 +98,8 @@ def test_fp8_shapes(shape):
     B, H, Hkv, N, d, causal = shape
     say(f"fa_fwd_fp8 {shape}")
     q8, k8, v8, scales, _ = fp8_inputs(B, H, Hkv, N, d, seed=401 + N)
-    scale = 1 / d ** 0.5
     go, gl = _run(q8, k8, v8, scales, causal)
-    _check_vs_oracle(q8, k8, v8, scales, causal, None, scale, go, gl)
-    _check_vs_exact(q8, k8, v8, scales, causal, None, scale, go)
+    _check(q8, k8, v8, scales, causal, None, 1 / d ** 0.5, go, gl)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -147,7 +114,7 @@ def test_fp8_padding_with_nan_codes(causal):
         for t in (q8, k8, v8):
             t[b, :, L:] = 0x7F
     go, gl = _run(q8, k8, v8, scales, causal, seq_lens=torch.tensor(lens, dtype=torch.int32))
-    _check_vs_oracle(*clean, scales, causal, lens, 1 / d ** 0.5, go, gl)
+    _check(*clean, scales, causal, lens, 1 / d ** 0.5, go, gl)
 
 
 def test_fp8_scale_zero_gives_mean_of_v():
@@ -161,20 +128,17 @@ def test_fp8_scale_zero_gives_mean_of_v():
 
 def test_fp8_workload_4k_full():
     w = WORKLOADS["fp8_4k"]
-    say("fa_fwd_fp8 fp8_4k full parity")
+    say("fa_fwd_fp8 fp8_4k, every row")
     q8, k8, v8, scales, _ = fp8_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], seed=w["seed"])
     go, gl = _run(q8, k8, v8, scales, w["causal"])
-    _check_vs_oracle(q8, k8, v8, scales, w["causal"], None, 1 / w["d"] ** 0.5, go, gl)
+    _check(q8, k8, v8, scales, w["causal"], None, 1 / w["d"] ** 0.5, go, gl)
 
 
 @pytest.mark.parametrize("name", ["fp8_16k", "fp8_16k_causal"])
-def test_fp8_workload_16k_sampled_rows(name):
+def test_fp8_workload_16k_every_query_tile(name):
     w = WORKLOADS[name]
-    say(f"fa_fwd_fp8 {name} sampled rows")
+    say(f"fa_fwd_fp8 {name}, a row of every 128-row query tile of every head")
     q8, k8, v8, scales, _ = fp8_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], seed=w["seed"])
     go, gl = _run(q8, k8, v8, scales, w["causal"])
-    N = w["N"]
-    rows = [0, 1, 63, 64, 255, 256, 4095, N // 2 + 17, N - 2, N - 1]
-    _check_vs_oracle(q8, k8, v8, scales, w["causal"], None, 1 / w["d"] ** 0.5,
-                     go[:, :, rows], gl[:, :, rows], rows=rows)
     assert np.isfinite(go).all() and np.isfinite(gl).all()
+    _check_sampled(q8, k8, v8, scales, w["causal"], 1 / w["d"] ** 0.5, go, gl, 128, w["seed"])

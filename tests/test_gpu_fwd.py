@@ -13,7 +13,7 @@ from io_aware_attention_02_amd import fa_fwd
 from io_aware_attention_02_amd.inputs import WORKLOADS, prefill_inputs
 from oracle import attention_ref
 
-from gpu_common import TOL_LSE, TOL_O_BF16, TOL_O_F32, device, f64, max_abs, say
+from gpu_common import TOL_LSE, TOL_O_BF16, TOL_O_F32, device, f64, max_abs, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -241,29 +241,40 @@ def test_prefill_4k_workload_full(seed):
     _check(q, k, v, o, lse, False, None, 1 / 128 ** 0.5, TOL_O_BF16)
 
 
-def _sample_rows(N, n=48, seed=0):
-    g = np.random.default_rng(seed)
-    fixed = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 129, N - 128, N - 65, N - 2, N - 1]
-    rows = set(r for r in fixed if 0 <= r < N) | set(g.integers(0, N, n).tolist())
-    return sorted(rows)
+def _check_every_tile(q, k, v, o, lse, causal, seq_lens, scale, tile, seed):
+    """One row of every `tile`-row query tile of every (batch, head), drawn per head, plus the
+    tile edges and, with per-sequence lengths, the rows around each length (padding fill
+    included)."""
+    B, H, N = q.shape[0], q.shape[1], q.shape[2]
+    group = H // k.shape[1]
+    for b in range(B):
+        for h in range(H):
+            rows = set(tile_rows(N, tile, h + H * b, seed))
+            if seq_lens is not None:
+                L = int(seq_lens[b])
+                rows |= {r for r in (L - 2, L - 1, L, L + 1) if 0 <= r < N}
+            rows = sorted(rows)
+            g = h // group
+            sl = None if seq_lens is None else seq_lens[b:b + 1]
+            _check(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                   o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], causal, sl, scale, TOL_O_BF16,
+                   rows=rows)
 
 
 @pytest.mark.parametrize("name", ["prefill_16k", "prefill_16k_causal"])
-def test_prefill_16k_workload_sampled(name):
+def test_prefill_16k_workload_every_query_tile(name):
     w = WORKLOADS[name]
-    say(f"fa_fwd {name} (sampled rows)")
+    say(f"fa_fwd {name}: a row of every 256-row query tile of every head")
     q, k, v, _ = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], "bf16", seed=w["seed"])
     o, lse = _run(q, k, v, w["causal"])
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    _check(q, k, v, o, lse, w["causal"], None, 1 / 128 ** 0.5, TOL_O_BF16, rows=_sample_rows(w["N"]))
+    _check_every_tile(q, k, v, o.cpu(), lse.cpu(), w["causal"], None, 1 / 128 ** 0.5, 256, w["seed"])
 
 
-def test_gqa_varlen_workload_sampled():
+def test_gqa_varlen_workload_every_query_tile():
     w = WORKLOADS["gqa_varlen_8k"]
-    say("fa_fwd GQA causal varlen B=4 H=32 Hkv=8 N=8192 (sampled rows)")
+    say("fa_fwd GQA causal varlen B=4 H=32 Hkv=8 N=8192: a row of every 256-row tile of every head")
     q, k, v, lens = prefill_inputs(w["B"], w["H"], w["Hkv"], w["N"], w["d"], "bf16", seed=w["seed"],
                                    len_lo=w["len_lo"], len_hi=w["len_hi"])
     o, lse = _run(q, k, v, True, lens)
-    rows = sorted(set(_sample_rows(w["N"], n=24)) | set(int(L) + dx for L in lens.tolist()
-                                                        for dx in (-2, -1, 0, 1) if 0 <= int(L) + dx < w["N"]))
-    _check(q, k, v, o, lse, True, lens, 1 / 128 ** 0.5, TOL_O_BF16, rows=rows)
+    _check_every_tile(q, k, v, o.cpu(), lse.cpu(), True, lens, 1 / 128 ** 0.5, 256, w["seed"])

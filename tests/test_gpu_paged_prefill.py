@@ -14,7 +14,7 @@ from io_aware_attention_02_amd import fa_paged_decode, fa_paged_prefill
 from io_aware_attention_02_amd.inputs import WORKLOADS, paged_prefill_inputs
 from oracle import paged_prefill_ref
 
-from gpu_common import TOL_LSE, TOL_O_BF16, device, f64, max_abs, say
+from gpu_common import TOL_LSE, TOL_O_BF16, device, f64, max_abs, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -102,17 +102,43 @@ def test_one_token_chunk_matches_decode():
     assert max_abs(f64(lse)[:, :, 0], f64(ld)) <= TOL_LSE
 
 
-def test_paged_prefill_workload_sampled_sequences():
+@pytest.mark.timeout(600)
+def test_paged_prefill_workload_every_sequence():
+    # All 16 sequences (contexts up to 32K, chunks up to 1024): one row of every 32-row block of
+    # each chunk (drawn per sequence; every wave of every query tile), the chunk's edges and the
+    # first padding rows, against the row-subset oracle.
     w = WORKLOADS["paged_prefill"]
-    say("fa_paged_prefill workload")
+    say("fa_paged_prefill workload, every sequence")
     q, kc, vc, table, sl, ql = paged_prefill_inputs(w["S"], w["Hq"], w["Hkv"], w["d"], w["max_q"],
                                                     w["block_size"], w["len_lo"], w["len_hi"],
                                                     seed=w["seed"])
     o, lse = _run(q, kc, vc, table, sl, ql)
-    # the three sequences with the least oracle work (L_b * Q_b); the rest are checked for finiteness
-    small = sorted(range(w["S"]), key=lambda b: int(sl[b]) * int(ql[b]))[:3]
-    _check(q, kc, vc, table, sl, ql, o, lse, 1 / w["d"] ** 0.5, seqs=small)
     assert torch.isfinite(o.float()).all()
+    _check_rows(q, kc, vc, table, sl, ql, o, lse, 1 / w["d"] ** 0.5, w["seed"])
+
+
+def _check_rows(q, kc, vc, table, lens, qlens, o, lse, scale, seed):
+    kcf, vcf = kc.float().numpy(), vc.float().numpy()
+    tb = table.numpy()
+    go, gl = f64(o), f64(lse)
+    Qmax = q.shape[2]
+    for b in range(q.shape[0]):
+        L, Q = int(lens[b]), int(qlens[b])
+        rows = set(tile_rows(Qmax, 32, b, seed))
+        rows |= {r for r in (0, Q - 2, Q - 1, Q, Q + 1, 127, 128) if 0 <= r < Qmax}
+        rows = sorted(rows)
+        ro, rl = paged_prefill_ref(f64(q[b:b + 1]), kcf, vcf, tb[b:b + 1], [L], [Q], scale,
+                                   rows=rows)
+        sel = np.asarray(rows) < Q
+        g_o, g_l = go[b][:, rows], gl[b][:, rows]
+        if sel.any():
+            eo = max_abs(g_o[:, sel], ro[0][:, sel])
+            el = max_abs(g_l[:, sel], rl[0][:, sel])
+            say(f"  seq {b} (L={L}, Q={Q}): O max-abs {eo:.2e}, LSE {el:.2e}")
+            assert eo <= TOL_O_BF16, f"seq {b} (L={L}, Q={Q}): O max-abs {eo:.3e}"
+            assert el <= TOL_LSE, f"seq {b} (L={L}, Q={Q}): LSE max-abs {el:.3e}"
+        assert (g_o[:, ~sel] == 0).all(), f"seq {b}: padding rows of O not zero"
+        assert np.isneginf(g_l[:, ~sel]).all(), f"seq {b}: padding rows of LSE not -inf"
 
 
 def test_paged_prefill_row_maximum_far_above_first_tile():
@@ -129,3 +155,36 @@ def test_paged_prefill_row_maximum_far_above_first_tile():
         kc[int(table[b, t // 16]), t % 16] = 4.0
     o, lse = _run(q, kc, vc, table, sl, ql)
     _check(q, kc, vc, table, sl, ql, o, lse, 1 / d ** 0.5)
+
+
+# Shared pool: the literal reading of a pool of 4096 physical blocks that every sequence draws
+# its ids from, with replacement -- ids repeat across sequences and inside one sequence.
+def test_paged_prefill_shared_pool_with_repeated_ids():
+    S, Hq, Hkv, d, Q = 4, 32, 8, 128, 300
+    lens, qls = [3000, 1200, 640, 5000], [300, 129, 64, 1]
+    say("fa_paged_prefill, 4096-block shared pool, ids drawn with replacement")
+    q, kc, vc, table, sl, ql = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=313, seq_lens=lens,
+                                                    q_lens=qls, pool_blocks=4096)
+    table[0, 7] = table[0, 3]          # the same block twice in one sequence, for certain
+    o, lse = _run(q, kc, vc, table, sl, ql)
+    _check(q, kc, vc, table, sl, ql, o, lse, 1 / d ** 0.5)
+
+
+def test_paged_prefill_block_ids_outside_the_pool_read_as_zeros():
+    # An id outside [0, num_blocks) is never dereferenced: that block's keys and values read as
+    # zeros.  The oracle sees the same table with those ids pointing at an all-zero block.
+    S, Hq, Hkv, d, Q = 2, 8, 2, 128, 100
+    lens, qls = [700, 300], [100, 40]
+    q, kc, vc, table, sl, ql = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=314, seq_lens=lens,
+                                                    q_lens=qls, spare_blocks=2)
+    P = kc.shape[0]
+    bad = table.clone()
+    bad[0, 5] = P                      # one past the pool
+    bad[1, 2] = -7                     # negative
+    o, lse = _run(q, kc, vc, bad, sl, ql)
+    kz = torch.cat([kc, torch.zeros_like(kc[:1])])
+    vz = torch.cat([vc, torch.zeros_like(vc[:1])])
+    ref_table = table.clone()
+    ref_table[0, 5] = P
+    ref_table[1, 2] = P
+    _check(q, kz, vz, ref_table, sl, ql, o, lse, 1 / d ** 0.5)

@@ -146,3 +146,24 @@ def test_row_subset_equals_full_query_gradient(causal, lens):
     sub, dk, dv = attention_bwd_ref(q, k, v, do, 0.3, causal=causal, seq_lens=lens, rows=rows)
     assert dk is None and dv is None
     np.testing.assert_allclose(sub, full[:, :, rows], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, [7, 10]), (True, [0, 9])])
+def test_key_subset_equals_full_key_gradients(causal, lens):
+    # dK, dV of selected keys (grouped heads summed, keys past a length zero) equal the same
+    # rows of the full computation, whichever way the query rows are blocked.
+    from oracle.backward import _dkdv_keys
+    rng = np.random.default_rng(30)
+    B, H, Hkv, N, d = 2, 6, 2, 10, 5
+    q, do = _rand(rng, B, H, N, d), _rand(rng, B, H, N, d)
+    k, v = _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, d)
+    _, fk, fv = attention_bwd_ref(q, k, v, do, 0.3, causal=causal, seq_lens=lens)
+    keys = [9, 0, 4, 7, 8]
+    dq, dk, dv = attention_bwd_ref(q, k, v, do, 0.3, causal=causal, seq_lens=lens, keys=keys)
+    assert dq is None
+    np.testing.assert_allclose(dk, fk[:, :, keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, fv[:, :, keys], rtol=0, atol=1e-13)
+    for blk in (1, 3, 4):
+        bk, bv = _dkdv_keys(q, k, v, do, 0.3, causal, lens, keys, row_block=blk)
+        np.testing.assert_allclose(bk, fk[:, :, keys], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(bv, fv[:, :, keys], rtol=0, atol=1e-13)

@@ -50,7 +50,9 @@ MUTANTS = [
     ("paged_decode_scale_dropped", "paged.py",
      "s = float(scale) * (kb[:, g, :] @ q[b, h])", "s = kb[:, g, :] @ q[b, h]"),
     ("chunk_offset_dropped", "paged.py",
-     "counts = (L - Q) + np.arange(Q) + 1", "counts = np.arange(Q) + 1"),
+     "counts = (L - Q) + sel[valid] + 1", "counts = sel[valid] + 1"),
+    ("chunk_rows_past_chunk_attend", "paged.py",
+     "valid = sel < Q\n", "valid = sel < L\n"),
     # backward
     ("bwd_row_term_sign", "backward.py",
      "            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))\n            dq[b, h, :L]",
@@ -63,6 +65,14 @@ MUTANTS = [
     ("bwd_row_subset_drops_row_term", "backward.py",
      "            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))\n            dq[b, h, valid]",
      "            ds = p * dp\n            dq[b, h, valid]"),
+    ("bwd_key_subset_row_term_sign", "backward.py",
+     "dsj = pj * (dpj - drow[:, None])", "dsj = pj * (dpj + drow[:, None])"),
+    ("bwd_key_subset_dk_scale_dropped", "backward.py",
+     "dk[b, g, valid] += scale * (dsj.T @ q[b, h, rows])", "dk[b, g, valid] += dsj.T @ q[b, h, rows]"),
+    ("bwd_key_subset_row_term_from_values", "backward.py",
+     "drow = (dob * o).sum(axis=1)", "drow = (dob * vb[rows]).sum(axis=1)"),
+    ("bwd_key_subset_dv_from_scores", "backward.py",
+     "dv[b, g, valid] += pj.T @ dob", "dv[b, g, valid] += dsj.T @ dob"),
     # FP8 form
     ("e4m3_ties_away_from_zero", "fp8.py",
      "up = (frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2) == 1))", "up = frac >= 0.5"),

@@ -377,3 +377,19 @@ def test_paged_prefill_of_one_token_is_a_decode_step():
     op, lp = paged_prefill_ref(q[:, :, None, :], kc, vc, table, lens, [1, 1, 1], 0.25)
     np.testing.assert_allclose(op[:, :, 0], od, atol=1e-12)
     np.testing.assert_allclose(lp[:, :, 0], ld, atol=1e-12)
+
+
+@pytest.mark.parametrize("rows", [[0, 5, 1], [2, 3, 4, 5]])
+def test_paged_prefill_row_subset_matches_full_rows(rows):
+    # Rows of each sequence's chunk (and rows past a chunk, which are padding) equal the same rows
+    # of the full computation.
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(57)
+    S, Hq, Hkv, d, bs = 4, 4, 2, 8, 4
+    lens, qls, Qmax = [13, 7, 16, 0], [5, 6, 1, 0], 6
+    _, kc, vc, table = _paged_case(rng, S, Hq, Hkv, d, bs, lens)
+    q = _rand(rng, S, Hq, Qmax, d)
+    o, l = paged_prefill_ref(q, kc, vc, table, lens, qls, 0.3)
+    os_, ls_ = paged_prefill_ref(q, kc, vc, table, lens, qls, 0.3, rows=rows)
+    np.testing.assert_array_equal(os_, o[:, :, rows])
+    np.testing.assert_array_equal(ls_, l[:, :, rows])
