@@ -422,6 +422,14 @@ def main():
     t_pre = sum(a.elapsed_time(b) for (a, b), _ in ev) / K      # ms
     t_dec = sum(a.elapsed_time(b) for _, (a, b) in ev) / K      # ms
 
+    # Host copies of what the timed calls computed (the extras below reuse these buffers), for
+    # the parity report of the cpu_baseline leg.
+    timed_out = None
+    if not args.no_cpu_baseline:
+        timed_out = {"fwd": (o.float().cpu().numpy(), lse.cpu().numpy()),
+                     "decode": (dq.cpu(), kc.cpu(), vc.cpu(), table.cpu(), lens_host,
+                                do.float().cpu().numpy(), dlse.cpu().numpy())}
+
     flops = acc.attention_flops(wf["B"], wf["H"], wf["N"], wf["d"], causal=False)
     tflops = flops / (t_pre * 1e-3) / 1e12
     dbytes = acc.decode_bytes(lens_host, wd["Hq"], wd["Hkv"], wd["d"], wd["block_size"])
@@ -579,10 +587,7 @@ def main():
         out["extras"] = extras
 
     if not args.no_cpu_baseline:
-        # Host copies of what the GPU computed, for the parity report of the baseline leg.
-        gpu = {"fwd": (o.float().cpu().numpy(), lse.cpu().numpy()),
-               "decode": (dq.cpu(), kc.cpu(), vc.cpu(), table.cpu(), lens_host,
-                          do.float().cpu().numpy(), dlse.cpu().numpy())}
+        gpu = dict(timed_out)
         for name in ("single_head_fp32", "prefill_4k"):
             ws_ = WORKLOADS[name]
             qs, ks, vs, _ = prefill_inputs(ws_["B"], ws_["H"], ws_["Hkv"], ws_["N"], ws_["d"],
