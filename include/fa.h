@@ -18,8 +18,9 @@
  *
  * Conventions for every entry point
  *   - Every data pointer is a caller-owned DEVICE pointer (e.g. from torch).  The library
- *     allocates nothing, keeps no state between calls, never synchronises the host and never
- *     prints.  It is safe to capture in a HIP graph.
+ *     allocates nothing, never synchronises the host and never prints.  It keeps no state
+ *     between calls, except the static device scratch behind fa_paged_decode_noalloc (held per
+ *     GPU for the life of the process).  It is safe to capture in a HIP graph.
  *   - Results are valid once the caller has synchronised `stream` (a hipStream_t; NULL means
  *     the default stream).
  *   - Errors are reported through the return value only.  Argument validation happens before
@@ -50,7 +51,9 @@ typedef enum fa_status {
                              workspace too small, ... */
   FA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dim not 64/128, unknown dtype,
                              block size not 16, query-group size above 16, ... */
-  FA_ERR_HIP = 3          /* the HIP runtime reported an error (no device, launch failure) */
+  FA_ERR_HIP = 3,         /* the HIP runtime reported an error (no device, launch failure) */
+  FA_ERR_TOO_LARGE = 4    /* fa_paged_decode_noalloc: the sizes need more than the library's
+                             static scratch (FA_DECODE_SCRATCH_BYTES) */
 } fa_status;
 
 /* Element type of q, k, v and o for fa_fwd. */
@@ -200,6 +203,32 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
                           float* lse, int num_seqs, int Hq, int Hkv, int d, int block_size,
                           int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Bytes of the static device scratch behind fa_paged_decode_noalloc (per GPU). */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)80 << 20)
+
+/*
+ * fa_paged_decode_noalloc -- fa_paged_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: the key-range partials go to a static device array of
+ * FA_DECODE_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends (its address is looked up once per device, on the first call there).  The call
+ * allocates nothing and runs the same kernels as fa_paged_decode, so the results are identical.
+ *
+ *   Arguments: as for fa_paged_decode, without workspace and workspace_bytes.
+ *   Sizes: fa_paged_decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size) must
+ *          not exceed FA_DECODE_SCRATCH_BYTES (80 MiB: e.g. 64 sequences x 32 query heads with
+ *          a 32768-token block table at d = 128), else FA_ERR_TOO_LARGE before any HIP call.
+ *   stream: must belong to the current device (else FA_ERR_HIP).
+ *   Calls on one GPU share the scratch: calls that overlap on it (different streams, or
+ *   different host threads without ordering) race and must not be issued.  Nothing in the
+ *   scratch needs to start at zero; it keeps the last call's partials.
+ */
+fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                  float* lse, int num_seqs, int Hq, int Hkv, int d,
+                                  int block_size, int max_blocks_per_seq, int num_blocks,
+                                  float scale, void* stream);
 
 /*
  * fa_paged_prefill -- chunked prefill against a paged KV cache.

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     fa_fwd_unfused,
     fa_fwd_unfused_workspace_bytes,
     fa_paged_decode,
+    fa_paged_decode_noalloc,
     fa_paged_decode_workspace_bytes,
     fa_paged_prefill,
     fa_status_str,

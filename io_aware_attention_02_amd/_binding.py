@@ -23,6 +23,7 @@ __all__ = [
     "fa_fwd_unfused",
     "fa_fwd_unfused_workspace_bytes",
     "fa_paged_decode",
+    "fa_paged_decode_noalloc",
     "fa_paged_decode_workspace_bytes",
     "fa_paged_prefill",
     "fa_status_str",
@@ -74,6 +75,9 @@ def load_library():
     lib.fa_paged_decode.restype = i32
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, sz, vp]
+    lib.fa_paged_decode_noalloc.restype = i32
+    lib.fa_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, i32, f32, vp]
     lib.fa_paged_prefill.restype = i32
     lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i32, f32, vp]
@@ -270,6 +274,36 @@ def fa_paged_decode(q, k_cache, v_cache, block_table, seq_lens, o=None, lse=None
                              _stream(stream))
     if st != 0:
         raise FaError(st, "fa_paged_decode")
+    return o, lse
+
+
+def fa_paged_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale=None,
+                            stream=None):
+    """fa_paged_decode without a workspace: the library keeps the partial results in its static
+    device scratch (FA_DECODE_SCRATCH_BYTES per GPU).  ``o`` [S,Hq,d] bf16 and ``lse`` [S,Hq]
+    fp32 (or None) are the caller's preallocated outputs; nothing is allocated here or in the
+    library.  Calls that overlap on one GPU race."""
+    lib = load_library()
+    _check_device_tensor("q", q, torch.bfloat16)
+    _check_device_tensor("k_cache", k_cache, torch.bfloat16)
+    _check_device_tensor("v_cache", v_cache, torch.bfloat16)
+    _check_device_tensor("block_table", block_table, torch.int32)
+    _check_device_tensor("seq_lens", seq_lens, torch.int32)
+    _check_device_tensor("o", o, torch.bfloat16)
+    if lse is not None:
+        _check_device_tensor("lse", lse, torch.float32)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape or block_table.dim() != 2:
+        raise ValueError("q [S,Hq,d], caches [P,bs,Hkv,d], block_table [S,M]")
+    S, Hq, d = q.shape
+    P, bs, Hkv, _ = k_cache.shape
+    M = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.fa_paged_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                     _ptr(seq_lens), _ptr(o), _ptr(lse), S, Hq, Hkv, d, bs, M, P,
+                                     float(scale), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_paged_decode_noalloc")
     return o, lse
 
 

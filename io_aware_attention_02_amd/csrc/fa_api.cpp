@@ -41,6 +41,8 @@ const char* fa_status_str(fa_status status) {
       return "unsupported configuration";
     case FA_ERR_HIP:
       return "HIP runtime error";
+    case FA_ERR_TOO_LARGE:
+      return "sizes exceed the static scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -250,53 +252,90 @@ size_t fa_paged_decode_workspace_bytes(int num_seqs, int Hq, int d, int max_bloc
   return fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);
 }
 
-fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_table, const int32_t* seq_lens, void* o,
-                          float* lse, int num_seqs, int Hq, int Hkv, int d, int block_size,
-                          int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !workspace)
-    return FA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both decode entry points (everything except the workspace) and the packed
+// launch arguments; returns FA_OK when the call may proceed.
+fa_status check_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                       int num_seqs, int Hq, int Hkv, int d, int block_size,
+                       int max_blocks_per_seq, int num_blocks, float scale, fa::DecodeArgs* a) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return FA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (block_size != 16) return FA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
-  // Grid: one 64-thread workgroup per (kv head, key range, sequence), at most one per 512 tokens, rounded up
-  // to a multiple of 8 ranges; the total thread count must fit a 32-bit grid.
+  // Grid: one 64-thread workgroup per (kv head, key range, sequence), at most one per 512
+  // tokens, rounded up to a multiple of 8 ranges; the total thread count must fit a 32-bit grid.
   if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_UNSUPPORTED;
   const long long splits = fa::decode_splits(max_blocks_per_seq, block_size);
   const long long units = ((long long)num_seqs * splits + 7) / 8 * 8;
   if (!product_at_most(INT_MAX, units, Hkv, 64)) return FA_ERR_UNSUPPORTED;
-  const size_t need =
-      fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size);
-  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_table = block_table;
+  a->seq_lens = seq_lens;
+  a->o = o;
+  a->lse = lse;
+  a->S = num_seqs;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->d = d;
+  a->block_size = block_size;
+  a->max_blocks = max_blocks_per_seq;
+  a->num_blocks = num_blocks;
+  a->scale = scale;
+  a->workspace = nullptr;
+  return FA_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* o,
+                          float* lse, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   fa::DecodeArgs a;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.o = o;
-  a.lse = lse;
-  a.S = num_seqs;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.d = d;
-  a.block_size = block_size;
-  a.max_blocks = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.scale = scale;
+  const fa_status st = check_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_seqs,
+                                    Hq, Hkv, d, block_size, max_blocks_per_seq, num_blocks, scale,
+                                    &a);
+  if (st != FA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size))
+    return FA_ERR_INVALID_ARG;
   a.workspace = workspace;
   const hipError_t e = fa::launch_paged_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                  float* lse, int num_seqs, int Hq, int Hkv, int d,
+                                  int block_size, int max_blocks_per_seq, int num_blocks,
+                                  float scale, void* stream) {
+  fa::DecodeArgs a;
+  const fa_status st = check_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_seqs,
+                                    Hq, Hkv, d, block_size, max_blocks_per_seq, num_blocks, scale,
+                                    &a);
+  if (st != FA_OK) return st;
+  if (fa::decode_workspace_bytes(num_seqs, Hq, d, max_blocks_per_seq, block_size) >
+      fa::kDecodeScratchBytes)
+    return FA_ERR_TOO_LARGE;
+  const hipError_t e = fa::launch_paged_decode_noalloc(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

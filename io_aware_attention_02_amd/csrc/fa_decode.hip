@@ -33,6 +33,8 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <mutex>
+
 namespace fa {
 namespace {
 
@@ -416,6 +418,48 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   return a.d == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The decode without a caller workspace: the split partials go to a static device array of
+// kDecodeScratchBytes, one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in for the symbol): the device
+// address of each GPU's copy is looked up once per device with hipGetSymbolAddress, with that
+// device current, and that address is the workspace the kernels get.  Every partial the merge
+// reads is written earlier in the same call, so nothing needs clearing.  Calls that overlap on
+// one GPU share the array and race.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+}  // namespace
+
+hipError_t launch_paged_decode_noalloc(DecodeArgs a, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (stream != nullptr) {  // the scratch copy used is the current device's
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    if (sd != dev) return hipErrorInvalidDevice;
+  }
+  std::call_once(scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (scratch_err[dev] != hipSuccess) return scratch_err[dev];
+  if (decode_workspace_bytes(a.S, a.Hq, a.d, a.max_blocks, a.block_size) > kDecodeScratchBytes)
+    return hipErrorInvalidValue;  // the entry point rejects these sizes before any HIP call
+  a.workspace = scratch_ptr[dev];
+  return launch_paged_decode(a, stream);
 }
 
 }  // namespace fa

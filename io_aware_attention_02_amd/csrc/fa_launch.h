@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa.h"
+
 namespace fa {
 
 struct FwdArgs {
@@ -117,5 +119,10 @@ int decode_splits(int max_blocks, int block_size);
 int decode_splits_of(int max_blocks, int block_size, int split);
 size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_size);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+// The decode with its partials in the library's static device scratch (a.workspace is ignored):
+// kDecodeScratchBytes per GPU, so decode_workspace_bytes(...) must not exceed it.
+constexpr size_t kDecodeScratchBytes = FA_DECODE_SCRATCH_BYTES;
+hipError_t launch_paged_decode_noalloc(DecodeArgs a, hipStream_t stream);
 
 }  // namespace fa

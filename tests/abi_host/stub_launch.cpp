@@ -38,4 +38,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_paged_decode_noalloc(DecodeArgs a, hipStream_t) {
+  stub::last = {"paged_decode_noalloc", a.S, a.Hq, a.Hkv, a.max_blocks, a.d, a.num_blocks};
+  return hipSuccess;
+}
+
 }  // namespace fa

@@ -181,6 +181,17 @@ void decode() {
   (void)fa_fwd_unfused_workspace_bytes(INT_MAX, INT_MAX, 65536);
 }
 
+void decode_noalloc() {
+  auto call = [](int S, int Hq, int Hkv, int mb, const void* q) {
+    return fa_paged_decode_noalloc(q, P(Bp), P(C), I(Dp), I(Dp + 4), P(E), F(E), S, Hq, Hkv, 128,
+                                   16, mb, 4096, 0.1f, nullptr);
+  };
+  CHECK("noalloc ok", call(64, 32, 8, 2048, P(A)), FA_OK, "paged_decode_noalloc");
+  CHECK("noalloc too large", call(64, 32, 8, 4096, P(A)), FA_ERR_TOO_LARGE, "");
+  CHECK("noalloc null q", call(64, 32, 8, 2048, nullptr), FA_ERR_INVALID_ARG, "");
+  CHECK("noalloc grid overflow", call(INT_MAX, 32, 8, 2048, P(A)), FA_ERR_UNSUPPORTED, "");
+}
+
 }  // namespace
 
 int main() {
@@ -190,6 +201,7 @@ int main() {
   unfused();
   prefill();
   decode();
+  decode_noalloc();
   for (int s = 0; s <= 4; ++s)
     if (fa_status_str((fa_status)s) == nullptr) ++failures;
   std::printf("%s (%d failures)\n", failures ? "FAILED" : "all validation checks hold", failures);

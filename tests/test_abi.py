@@ -13,7 +13,7 @@ from io_aware_attention_02_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
-OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, HIPERR, TOO_LARGE = 0, 1, 2, 3, 4
 P = 0x100000  # a 16-byte-aligned stand-in for a device pointer; never dereferenced here
 
 
@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_fp8",
                                      "fa_fwd_unfused",
                                      "fa_fwd_unfused_workspace_bytes", "fa_paged_decode",
+                                     "fa_paged_decode_noalloc",
                                      "fa_paged_decode_workspace_bytes", "fa_paged_prefill",
                                      "fa_status_str"]
 
@@ -49,6 +50,7 @@ def test_status_strings(lib):
     assert _binding.fa_status_str(INVALID) == "invalid argument"
     assert _binding.fa_status_str(UNSUPPORTED) == "unsupported configuration"
     assert _binding.fa_status_str(HIPERR) == "HIP runtime error"
+    assert "static scratch" in _binding.fa_status_str(TOO_LARGE)
     assert _binding.fa_status_str(99) == "unknown status"
 
 
@@ -214,6 +216,34 @@ def test_decode_rejects(lib, kw, status):
     assert _dec(lib, **kw) == status
 
 
+def _dec_noalloc(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, S=4, Hq=32, Hkv=8, d=128, bs=16, M=64,
+             nb=256, scale=0.1, stream=None)
+    a.update(kw)
+    return lib.fa_paged_decode_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"],
+                                       a["lse"], a["S"], a["Hq"], a["Hkv"], a["d"], a["bs"],
+                                       a["M"], a["nb"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(bt=None), INVALID), (dict(o=None), INVALID),
+    (dict(S=0), INVALID), (dict(nb=0), INVALID), (dict(Hq=32, Hkv=5), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(kc=P + 8), INVALID), (dict(sl=P + 2), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(bs=32), UNSUPPORTED), (dict(Hq=64, Hkv=2), UNSUPPORTED),
+    (dict(S=1 << 20, M=1 << 14), UNSUPPORTED),
+    # 64 sequences x 32 heads with a 65536-token table need 144 MB of partials: over 80 MiB
+    (dict(S=64, Hq=32, M=4096), TOO_LARGE),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    assert _dec_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_limit_is_the_documented_scratch(lib):
+    # The decode workload (64 sequences x 32 heads, 32768-token tables, d = 128) fits the scratch.
+    assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 2048, 16) <= 80 << 20
+    assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 4096, 16) > 80 << 20
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
 def test_valid_call_without_a_device_reports_hip_error(lib):
     # Arguments pass validation, so the call reaches the runtime, which has no device.
@@ -223,6 +253,7 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     assert _pre(lib) == HIPERR
     assert _unf(lib) == HIPERR
     assert _fp8(lib) == HIPERR
+    assert _dec_noalloc(lib) == HIPERR
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
