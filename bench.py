@@ -66,14 +66,16 @@ def _time_calls(torch, fn, iters, warmup=3):
 
 
 class ClockSampler:
-    """Samples the GPU's engine (gfx) clock with amdsmi from a background thread while the
-    timed region runs (the main thread waits in a device synchronisation meanwhile).  The
-    published peaks assume the maximum clock; the clock held under load is recorded beside the
-    throughput.  Reports None with the reason if amdsmi cannot read the device."""
+    """Samples the GPU's engine (gfx) clock and socket power with amdsmi from a background
+    thread while the main thread keeps the GPU busy (it waits in device synchronisations
+    meanwhile).  The published peaks assume the maximum clock; the clock held under load is
+    recorded beside the throughput.  The driver's metrics refresh about once a second, so the
+    window must last a few seconds.  Reports None with the reason if amdsmi cannot read the
+    device."""
 
-    def __init__(self, torch, period_s=0.002):
+    def __init__(self, torch, period_s=0.1):
         import threading
-        self.samples, self.error, self.max_mhz = [], None, None
+        self.samples, self.power, self.error, self.max_mhz = [], [], None, None
         self._stop = threading.Event()
         self._period = period_s
         self._handle = None
@@ -100,17 +102,19 @@ class ClockSampler:
     def _read(self):
         m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
         per_xcd = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float))]
-        if per_xcd:
-            return sum(per_xcd) / len(per_xcd)
-        cur = m.get("current_gfxclk")
-        return cur if isinstance(cur, (int, float)) else None
+        clk = sum(per_xcd) / len(per_xcd) if per_xcd else m.get("current_gfxclk")
+        pw = m.get("current_socket_power")
+        return (clk if isinstance(clk, (int, float)) else None,
+                pw if isinstance(pw, (int, float)) else None)
 
     def _run(self):
         while not self._stop.is_set():
             try:
-                v = self._read()
-                if v is not None:
-                    self.samples.append(float(v))
+                clk, pw = self._read()
+                if clk is not None:
+                    self.samples.append(float(clk))
+                if pw is not None:
+                    self.power.append(float(pw))
             except Exception as e:  # noqa: BLE001
                 self.error = f"{type(e).__name__}: {e}"
                 return
@@ -127,15 +131,27 @@ class ClockSampler:
             self._thread.join()
         return False
 
-    def report(self):
+    def report(self, what):
         if not self.samples:
             return {"mhz_median": None, "samples": 0,
-                    "note": self.error or "no clock sample during the timed region"}
+                    "note": self.error or "no clock sample during the window"}
         s = sorted(self.samples)
+        pw = sorted(self.power)
         return {"mhz_median": round(s[len(s) // 2], 1), "mhz_min": round(s[0], 1),
                 "mhz_max": round(s[-1], 1), "samples": len(s), "max_engine_mhz": self.max_mhz,
-                "source": "amdsmi gpu metrics (current gfx clock, mean over XCDs) during the "
-                          "timed steps"}
+                "socket_power_w_median": round(pw[len(pw) // 2], 1) if pw else None,
+                "source": f"amdsmi gpu metrics every 0.1 s (gfx clock, mean over the XCDs) {what}"}
+
+
+def clock_under_load(torch, fn, seconds=2.5):
+    """Engine clock while fn() runs back to back for about `seconds`."""
+    with ClockSampler(torch) as clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+    return clock
 
 
 def _err(got, ref):
@@ -408,17 +424,16 @@ def main():
     K = args.steps
     ev = [(_events(torch), _events(torch)) for _ in range(K)]
     torch.cuda.synchronize()
-    with ClockSampler(torch) as clock:
-        t0 = time.perf_counter()
-        for (pa, pb), (da, db) in ev:
-            pa.record()
-            prefill()
-            pb.record()
-            da.record()
-            decode()
-            db.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for (pa, pb), (da, db) in ev:
+        pa.record()
+        prefill()
+        pb.record()
+        da.record()
+        decode()
+        db.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     t_pre = sum(a.elapsed_time(b) for (a, b), _ in ev) / K      # ms
     t_dec = sum(a.elapsed_time(b) for _, (a, b) in ev) / K      # ms
 
@@ -429,6 +444,10 @@ def main():
         timed_out = {"fwd": (o.float().cpu().numpy(), lse.cpu().numpy()),
                      "decode": (dq.cpu(), kc.cpu(), vc.cpu(), table.cpu(), lens_host,
                                 do.float().cpu().numpy(), dlse.cpu().numpy())}
+
+    # The metrics the clock is read from refresh about once a second, longer than the timed
+    # steps, so the clock is taken over a window of the same forward right after them.
+    clock = clock_under_load(torch, prefill)
 
     flops = acc.attention_flops(wf["B"], wf["H"], wf["N"], wf["d"], causal=False)
     tflops = flops / (t_pre * 1e-3) / 1e12
@@ -470,7 +489,8 @@ def main():
             "ms_per_launch": round(t_pre, 4),
             "flops_per_launch": flops,
         },
-        "engine_clock": clock.report(),
+        "engine_clock": clock.report("over 2.5 s of the same forward right after the timed "
+                                     "steps"),
         "decode": {
             "value": round(gbps, 1),
             "unit": "GB/s",

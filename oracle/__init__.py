@@ -14,9 +14,13 @@ fusion, no online softmax), except for the FP8 variant:
                            fixed-size physical blocks addressed through a block table.
 * ``paged_prefill_ref`` -- the newest Q_b tokens of each sequence (chunked prefill) against the
                            same paged cache, causal with the offset L_b - Q_b.
-* ``attention_fp8_ref`` -- FP8 (e4m3) inputs with per-tensor scales, online softmax over key
-                           blocks with the probabilities rounded to e4m3 for the P V product
-                           (an approximation, so it follows the algorithm's steps).
+* ``e4m3_decode``       -- the real values of FP8 (e4m3) codes; the FP8 path's parity oracle
+                           is the exact attention (``attention_probs_ref``) of the decoded,
+                           descaled tensors.
+* ``attention_fp8_ref`` -- a model of rounding the probabilities to e4m3 inside an online
+                           softmax over key blocks (not the FP8 parity oracle: tests use it to
+                           show that the tolerance derived from the e4m3 format admits such
+                           rounding schemes).
 * ``attention_bwd_ref`` -- gradients of the prefill definition with respect to Q, K and V
                            (chain rule through the row softmax, full P materialised).
 

@@ -1,8 +1,15 @@
-"""FP8 (e4m3) attention forward in float64 (oracle; test infrastructure).
+"""FP8 (e4m3) decoding, rounding, and a float64 model of rounded-probability attention
+(oracle; test infrastructure).
 
 The pages name FP8 as the main addition of FlashAttention V3 (the "GPU优化" tag page,
 guijiagi.com, excerpt "注意力计算的性能瓶颈", part Flash Attention V3: FP8 tensor cores and an
-asynchronous pipeline on the H100) without fixing the arithmetic.  The reading taken here:
+asynchronous pipeline on the H100) without fixing the arithmetic.  What the FP8 path computes is
+the exact attention of the dequantised tensors; its parity oracle is that definition (decode the
+codes with ``e4m3_decode``, multiply by the descales, then the exact attention of
+``attention.py``), and the tolerance against it is derived from the e4m3 format.  The function
+``attention_fp8_ref`` below is NOT that oracle: it is a model of one way to round the
+probabilities to e4m3 inside an online softmax, kept to check on the CPU that the derived
+tolerance admits such rounding schemes (and rejects mistakes).  Its reading:
 
 * Inputs are FP8 e4m3 codes (the OCP "fn" variant: 4 exponent bits with bias 7, 3 mantissa
   bits, no infinities, max 448) with one float descale factor per tensor: the real value of a
@@ -19,9 +26,10 @@ asynchronous pipeline on the H100) without fixing the arithmetic.  The reading t
   unrounded p, so the LSE is the exact log-sum-exp of the scaled scores.
 
 Because the rounding of p happens relative to the running maximum of each block, the result
-depends on the block size; ``block`` must equal the fused kernel's softmax block (64 keys).  With
-``p_scale=None`` nothing is rounded and the function is the exact attention of the dequantised
-inputs (pinned against the three-pass oracle).
+depends on the block size and the lag; the model takes both as arguments, and any choice is one
+admissible rounding scheme, not a specification of a kernel.  With ``p_scale=None`` nothing is
+rounded and the function is the exact attention of the dequantised inputs (pinned against the
+three-pass oracle).
 
 e4m3 decoding and rounding are written out from the format's definition (no library cast).
 """
