@@ -332,13 +332,16 @@ def only(args, torch, dev, wf, wd):
         fn = lambda: fa_bwd(q, k, v, o, lse, dout, gq, gk, gv)  # noqa: E731
         what = "fa_bwd B=1 H=8 N=16384 d=128 bf16 non-causal"
     elif args.only == "prefill_paged":
-        from io_aware_attention_02_amd import fa_paged_prefill
+        from io_aware_attention_02_amd import fa_paged_prefill, fa_paged_prefill_workspace_bytes
         from io_aware_attention_02_amd.inputs import WORKLOADS, paged_prefill_inputs
         w5 = WORKLOADS["paged_prefill"]
         ts = paged_prefill_inputs(w5["S"], w5["Hq"], w5["Hkv"], w5["d"], w5["max_q"],
                                   w5["block_size"], w5["len_lo"], w5["len_hi"], seed=w5["seed"])
         pq, pkc, pvc, ptb, psl, pql = (t.to(dev) for t in ts)
-        fn = lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql)  # noqa: E731
+        pws = torch.empty(fa_paged_prefill_workspace_bytes(w5["S"], w5["max_q"], w5["Hq"], w5["Hkv"],
+                                                           w5["d"], ptb.shape[1]),
+                          dtype=torch.uint8, device=dev)
+        fn = lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql, workspace=pws)  # noqa: E731
         what = "fa_paged_prefill 16 seqs, chunks <= 1024 of contexts U[1024,32768], Hq=32 Hkv=8"
     elif args.only == "decode":
         dq, kc, vc, table, lens = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
@@ -562,8 +565,10 @@ def main():
             extras[name] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2),
                             "fused_speedup": round(t / t_fused, 2)}
             del wsu
-        # Chunked prefill against the paged cache (16 sequences, chunks of up to 1024 tokens).
-        from io_aware_attention_02_amd import fa_paged_prefill
+        # Chunked prefill against the paged cache (16 sequences, chunks of up to 1024 tokens),
+        # then the same contexts with every chunk cut to at most 128 tokens (short chunks against
+        # long contexts: the key loops are split over several workgroups and merged).
+        from io_aware_attention_02_amd import fa_paged_prefill, fa_paged_prefill_workspace_bytes
         from io_aware_attention_02_amd.inputs import paged_prefill_inputs
         w5 = WORKLOADS["paged_prefill"]
         pq, pkc, pvc, ptb, psl, pql = paged_prefill_inputs(
@@ -573,9 +578,19 @@ def main():
         pq, pkc, pvc, ptb, psl, pql = (t.to(dev) for t in (pq, pkc, pvc, ptb, psl, pql))
         po = torch.empty_like(pq)
         pl = torch.empty(pq.shape[:3], dtype=torch.float32, device=dev)
-        t = _time_calls(torch, lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql, po, pl), 10)
+        pws = torch.empty(fa_paged_prefill_workspace_bytes(w5["S"], w5["max_q"], w5["Hq"], w5["Hkv"],
+                                                           w5["d"], ptb.shape[1]),
+                          dtype=torch.uint8, device=dev)
+        t = _time_calls(torch, lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql, po, pl,
+                                                        workspace=pws), 10)
         extras["paged_prefill"] = {"ms": round(t, 4), "TFLOP/s": round(f / t / 1e9, 2)}
-        del pkc, pvc
+        pql128 = torch.clamp(pql, max=128)
+        f128 = acc.paged_prefill_flops(psl.tolist(), pql128.tolist(), w5["Hq"], w5["d"])
+        t = _time_calls(torch, lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql128, po, pl,
+                                                        workspace=pws), 10)
+        extras["paged_prefill_chunks_le_128"] = {"ms": round(t, 4),
+                                                 "TFLOP/s": round(f128 / t / 1e9, 2)}
+        del pkc, pvc, pws
         # Backward (recompute from the forward's LSE) on the headline inputs, both masks.
         from io_aware_attention_02_amd import fa_bwd, fa_bwd_workspace_bytes
         from io_aware_attention_02_amd.inputs import output_gradient

@@ -231,6 +231,16 @@ fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void
                                   float scale, void* stream);
 
 /*
+ * fa_paged_prefill_workspace_bytes -- size in bytes of the device workspace fa_paged_prefill
+ * needs for these sizes: the work plan (a few ints per sequence and per work item) and the
+ * partial results of split key ranges, whose number is bounded by a constant (2048 slots of 128
+ * query rows x (d + 2) floats: 130 MiB at d = 128, 66 MiB at d = 64) whatever the lengths.
+ * Returns 0 for non-positive sizes or Hq not a multiple of Hkv.
+ */
+size_t fa_paged_prefill_workspace_bytes(int num_seqs, int max_q, int Hq, int Hkv, int d,
+                                        int max_blocks_per_seq);
+
+/*
  * fa_paged_prefill -- chunked prefill against a paged KV cache.
  *
  * For each sequence b the query chunk is its newest Q_b = q_lens[b] tokens, at positions
@@ -238,8 +248,12 @@ fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void
  * in the cache.  Query row i attends to the cached tokens 0 .. L_b - Q_b + i (causal with that
  * offset) -- the chunked prefill of the LLM inference-optimisation article (ijyty.com) §3.2, a
  * long prompt processed piece by piece against the cache built so far; Q_b = 1 is one decode
- * step.  The cache and block table are as for fa_paged_decode; the kernel is fa_fwd's, with its
- * key/value tiles gathered block by block through the table.
+ * step.  The cache and block table are as for fa_paged_decode; the arithmetic is fa_fwd's, with
+ * the key/value tiles gathered block by block through the table.  A small planning kernel reads
+ * the lengths on the device and lays out the work; key ranges much longer than the average
+ * work per compute unit are split and their partial results merged exactly (the block merge of
+ * the online softmax, "FlashAttention优化" §3.2.2), so the result does not depend on the split
+ * beyond floating-point rounding.
  *
  *   q            [num_seqs, Hq, max_q, d] bf16 (head-major, as fa_fwd's q); rows i >= Q_b are
  *                padding
@@ -250,13 +264,17 @@ fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void
  *   o            [num_seqs, Hq, max_q, d] bf16, written (0 in padding rows)
  *   lse          [num_seqs, Hq, max_q] fp32, written (natural log; -inf in padding rows)
  *   Hq % Hkv == 0.  d: 64 or 128.  block_size: 16.  scale finite and >= 0.
- *   stream       hipStream_t or NULL.
+ *   workspace    device buffer of at least fa_paged_prefill_workspace_bytes(num_seqs, max_q,
+ *                Hq, Hkv, d, max_blocks_per_seq) bytes, 16-byte aligned, owned by the caller;
+ *                its contents on entry do not matter (smaller: FA_ERR_INVALID_ARG).
+ *   stream       hipStream_t or NULL.  Calls that share a workspace must be ordered.
  */
 fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* q_lens, void* o, float* lse, int num_seqs, int max_q,
                            int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
-                           int num_blocks, float scale, void* stream);
+                           int num_blocks, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * fa_fwd_unfused_workspace_bytes -- bytes of the workspace fa_fwd_unfused needs: the N x N

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     fa_paged_decode_noalloc,
     fa_paged_decode_workspace_bytes,
     fa_paged_prefill,
+    fa_paged_prefill_workspace_bytes,
     fa_status_str,
     library_path,
     load_library,

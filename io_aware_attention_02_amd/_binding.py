@@ -26,6 +26,7 @@ __all__ = [
     "fa_paged_decode_noalloc",
     "fa_paged_decode_workspace_bytes",
     "fa_paged_prefill",
+    "fa_paged_prefill_workspace_bytes",
     "fa_status_str",
     "library_path",
     "load_library",
@@ -80,7 +81,9 @@ def load_library():
                                             i32, i32, f32, vp]
     lib.fa_paged_prefill.restype = i32
     lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                     i32, i32, f32, vp]
+                                     i32, i32, f32, vp, sz, vp]
+    lib.fa_paged_prefill_workspace_bytes.restype = sz
+    lib.fa_paged_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_fwd_unfused_workspace_bytes.restype = sz
     lib.fa_fwd_unfused_workspace_bytes.argtypes = [i32, i32, i32]
     lib.fa_fwd_unfused.restype = i32
@@ -307,11 +310,18 @@ def fa_paged_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, 
     return o, lse
 
 
+def fa_paged_prefill_workspace_bytes(S, Qmax, Hq, Hkv, d, M):
+    return int(load_library().fa_paged_prefill_workspace_bytes(int(S), int(Qmax), int(Hq), int(Hkv),
+                                                               int(d), int(M)))
+
+
 def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, q_lens, o=None, lse=None,
-                     scale=None, stream=None):
+                     scale=None, workspace=None, stream=None):
     """Chunked prefill against a paged cache.  q [S,Hq,Qmax,d] bf16 (each sequence's newest
     q_lens[b] tokens, head-major); caches [P,bs,Hkv,d] bf16; block_table [S,M], seq_lens [S],
-    q_lens [S] int32.  Returns (o [S,Hq,Qmax,d] bf16, lse [S,Hq,Qmax] fp32)."""
+    q_lens [S] int32.  Returns (o [S,Hq,Qmax,d] bf16, lse [S,Hq,Qmax] fp32).  ``workspace``:
+    optional uint8 device tensor of fa_paged_prefill_workspace_bytes(S, Qmax, Hq, Hkv, d, M)
+    bytes (allocated with torch if None)."""
     lib = load_library()
     _check_device_tensor("q", q, torch.bfloat16)
     _check_device_tensor("k_cache", k_cache, torch.bfloat16)
@@ -331,9 +341,14 @@ def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, q_lens, o=None,
     _check_device_tensor("lse", lse, torch.float32)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        need = fa_paged_prefill_workspace_bytes(S, Qmax, Hq, Hkv, d, M) if Hkv > 0 else 0
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_device_tensor("workspace", workspace)
     st = lib.fa_paged_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                               _ptr(seq_lens), _ptr(q_lens), _ptr(o), _ptr(lse), S, Qmax, Hq, Hkv,
-                              d, bs, M, P, float(scale), _stream(stream))
+                              d, bs, M, P, float(scale), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_paged_prefill")
     return o, lse

@@ -155,12 +155,19 @@ fa_status fa_fwd_unfused(const void* q, const void* k, const void* v, void* o, f
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_paged_prefill_workspace_bytes(int num_seqs, int max_q, int Hq, int Hkv, int d,
+                                        int max_blocks_per_seq) {
+  return fa::paged_prefill_workspace_bytes(num_seqs, max_q, Hq, Hkv, d, max_blocks_per_seq);
+}
+
 fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* q_lens, void* o, float* lse, int num_seqs, int max_q,
                            int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
-                           int num_blocks, float scale, void* stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !q_lens || !o || !lse)
+                           int num_blocks, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !q_lens || !o || !lse ||
+      !workspace)
     return FA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || max_q <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
@@ -170,15 +177,18 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(q_lens) & 3u) ||
-      (reinterpret_cast<uintptr_t>(lse) & 3u))
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || !aligned16(workspace))
     return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (block_size != 16) return FA_ERR_UNSUPPORTED;
-  // One workgroup per (sequence, query head, tile of >= 128 query rows); key positions and
-  // offsets in 32-bit integers.
-  if (max_q > kMaxN || !product_at_most(INT_MAX, num_seqs, Hq, (max_q + 127) / 128) ||
-      (long long)max_blocks_per_seq * block_size > kMaxN)
+  // Key positions and offsets in 32-bit integers; the work items (sequence x kv head x head
+  // subset x query block, at least 32 rows per block) indexed by 32-bit integers, 8 per item.
+  if (max_q > kMaxN || (long long)max_blocks_per_seq * block_size > kMaxN ||
+      !product_at_most(INT_MAX / 16, num_seqs, Hq, (max_q + 31) / 32))
     return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes <
+      fa::paged_prefill_workspace_bytes(num_seqs, max_q, Hq, Hkv, d, max_blocks_per_seq))
+    return FA_ERR_INVALID_ARG;
 
   fa::PagedPrefillArgs a;
   a.q = q;
@@ -197,6 +207,7 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.scale = scale;
+  a.workspace = workspace;
   const hipError_t e = fa::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

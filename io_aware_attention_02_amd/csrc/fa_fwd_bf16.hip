@@ -43,6 +43,7 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 #include "fa_tiles.h"
+#include "fa_softmax.h"
 
 #include <type_traits>
 
@@ -51,80 +52,32 @@ namespace {
 
 constexpr int kCUs = 256;              // compute units of an MI355X
 constexpr int kXcds = 8;               // accelerator complex dies (each with its own L2)
-constexpr float kTau = 16.f;           // headroom of the fixed reference (log2 units)
-constexpr float kMaxProb = 65536.f;    // 2^kTau
 
 struct Params {
   const bf16* q;
-  const bf16* k;  // paged: the key cache [num_blocks, 16, Hkv, d]
-  const bf16* v;  // paged: the value cache
+  const bf16* k;
+  const bf16* v;
   bf16* o;
   float* lse;
-  const int32_t* seq_lens;  // paged: tokens in the cache per sequence
-  const int32_t* table;     // paged: block table [B, max_blocks]
-  const int32_t* q_lens;    // paged: query rows per sequence (its newest tokens)
-  int H, group, Hkv, N, n_qt, total, max_blocks;
-  int num_blocks;  // paged: blocks in the pool; ids outside [0, num_blocks) are never dereferenced
+  const int32_t* seq_lens;  // valid rows per sequence, or nullptr
+  int H, group, Hkv, N, n_qt, total;
   float sl2;  // scale * log2(e): scores go to the exponent base 2
 };
 
-constexpr int kPageRows = 16;  // tokens per physical block of the paged cache
-
-// Per-lane byte offsets of this wave's direct loads when the tile rows come from a paged cache:
-// tile row r lives at slot r % 16 of its block, rows of one block are Hkv * d elements apart,
-// and the chunk swizzle is the tile's (by tile row).  Each load covers rows of one block.
-template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void tile_offsets_paged(int* off, int wave, int lane, int row_elems) {
-  using G = Geo<D>;
-  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
-#pragma unroll
-  for (int t = 0; t < NI_W; ++t) {
-    const int row = (wave * NI_W + t) * G::RPI + lane / G::CPR;
-    const int chunk = (lane % G::CPR) ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
-    off[t] = (row % kPageRows) * row_elems * 2 + chunk * 16;
-  }
-}
-
-// Direct global -> LDS copy of this wave's rows of one tile from a paged cache: all of them lie
-// in one physical block (bid), whose buffer resource ends at the sequence's last valid token.
-template <int D, int NW>
-__device__ __forceinline__ void load_tile_paged(lds_t* dst, const bf16* cache, int bid, int g,
-                                                int valid_rows, int Hkv, const int* off, int wave) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NI_W = LoadGeo<D, NW>::NI_W;
-  const int bytes = __builtin_amdgcn_readfirstlane(
-      valid_rows > 0 ? ((valid_rows - 1) * Hkv * D + D) * 2 : 0);
-  const uintptr_t base = reinterpret_cast<uintptr_t>(
-      cache + ((size_t)bid * kPageRows * Hkv + g) * D);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
-#pragma unroll
-  for (int t = 0; t < NI_W; ++t)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (wave * NI_W + t) * 1024, 16, off[t],
-                                             0, 0, 0);
-#endif
-}
-
-// With per-sequence lengths (varlen prefill, paged chunked prefill): the sequence a workgroup
-// serves, taken in order of decreasing key length L (ties by index).  A workgroup's cost grows
-// with the keys its rows see, up to L, so the sequences holding the heaviest workgroups start
-// first and the light ones fill in behind them.  (Ranking by a sequence's total work, L times its
-// query rows, would put a long context with a short chunk -- one very heavy workgroup -- near
-// the end of the grid.)  For the contiguous forward the query rows are the keys, so this is also
-// the order of total work.  Every workgroup ranks the sequences itself, one thread per sequence
+// With per-sequence lengths (varlen prefill): the sequence a workgroup serves, taken in order of
+// decreasing length L (ties by index), which is also the order of total work, so the sequences
+// holding the heaviest workgroups start first and the light ones fill in behind them.  Every workgroup ranks the sequences itself, one thread per sequence
 // against lengths staged in LDS; with more than kMaxRanked sequences the natural order is kept.
 // The order changes no result.
 constexpr int kMaxRanked = 512;
-template <int NW, bool PAGED>
+template <int NW>
 __device__ int by_work(const Params& p, int pos, int* buf) {
   const int S = p.total / (p.H * p.n_qt);
   if (S > kMaxRanked) return pos;
   int* w = buf;                   // key length of each sequence
   int* order = buf + kMaxRanked;  // sequence at each rank
   for (int i = threadIdx.x; i < S; i += 64 * NW)
-    w[i] = min(max(p.seq_lens[i], 0), PAGED ? p.max_blocks * kPageRows : p.N);
+    w[i] = min(max(p.seq_lens[i], 0), p.N);
   __syncthreads();
   for (int i = threadIdx.x; i < S; i += 64 * NW) {
     int r = 0;
@@ -135,90 +88,16 @@ __device__ int by_work(const Params& p, int pos, int* buf) {
   return order[pos];
 }
 
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
-  float m0 = s[0][0], m1 = s[1][0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) {
-    m0 = fmaxf(m0, s[0][r]);
-    m1 = fmaxf(m1, s[1][r]);
-  }
-  return max_xor32(fmaxf(m0, m1));
-}
-
-// Probabilities of one 16-key chunk (jj) of the tile: exp2(s * sl2 - m), packed to bf16 in the
-// k-slot order of the P^T operand; their sum is added to rs.  On masked tiles a masked score
-// (-inf) gives exactly 0 even when the scale is 0 (where -inf * 0 would be NaN).
-template <bool MASKED>
-__device__ __forceinline__ bf16x8 chunk_probs(const f32x16 (&s)[2], int jj, float sl2, float m_use,
-                                              float& rs) {
-  float e[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float x = s[jj >> 1][8 * (jj & 1) + t];
-    float arg = fmaf(x, sl2, -m_use);
-    if (MASKED && x == kNegInf) arg = kNegInf;
-    e[t] = fast_exp2(arg);
-  }
-  rs += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-  return pack_bf16x8(e);
-}
-
-// Softmax and O^T (d x 32 queries) = alpha O^T + V_tile^T P^T, interleaved.  The MFMAs run
-// chunk by chunk (16 keys) over the D/32 output blocks, each fed by two transposing V reads
-// kAheadV MFMAs ahead.  While they run, the vector ALU rescales the output blocks not yet
-// touched (alpha) and computes the next chunk's probabilities, so most of the softmax hides
-// under the matrix work.  Returns this lane's part of the tile's row sum.
-constexpr int kAheadV = 4;
-template <int D, bool MASKED, bool RESCALE>
-__device__ __forceinline__ float softmax_pv(f32x16 (&acc)[D / 32], const lds_t* Vb,
-                                            const FragAddr<D>& fa, const f32x16 (&s)[2],
-                                            float sl2, float m_use, float alpha) {
-  using G = Geo<D>;
-  constexpr int NM = 4 * G::NB;
-  float rs = 0.f;
-  __builtin_amdgcn_sched_barrier(0);
-  bf16x8 pf[4];
-  pf[0] = chunk_probs<MASKED>(s, 0, sl2, m_use, rs);
-  if (RESCALE) acc[0] *= alpha;
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-    for (int n = 0; n < G::NB; ++n) {
-      const lds_t* p = Vb + fa.v[n] + jj * 16 * G::RB;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * G::RB));
-      const bf16x8 vf = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      if (RESCALE && jj == 0 && n + 1 < G::NB) acc[n + 1] *= alpha;
-      acc[n] = mfma32(vf, pf[jj], acc[n]);
-    }
-    if (jj + 1 < 4) pf[jj + 1] = chunk_probs<MASKED>(s, jj + 1, sl2, m_use, rs);
-  }
-  // Schedule: the first reads, then per MFMA a few vector instructions and the next reads.
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAheadV, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
-    if (i + kAheadV < NM) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(0);
-  return rs;
-}
-
 // NG = 1: the NW waves own NW * 32 query rows and share every K/V tile.  NG = 2 (grids too
 // small to give each SIMD two waves otherwise): the waves form two groups of NW / 2 over the
 // same NW / 2 * 32 rows; group g takes the key tiles t with t % 2 == g, with its own LDS
 // buffers, and the two partial results (output, reference maximum, row sum) are combined
 // exactly at the end, as the online softmax combines any two blocks of keys
 // ("FlashAttention优化" §3.2.2).
-template <int D, bool CAUSAL, int NW, bool PAGED, int NG = 1>
+template <int D, bool CAUSAL, int NW, int NG = 1>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(Params p) {
-  static_assert(NG == 1 || (NG == 2 && !PAGED), "key groups are for contiguous K/V");
+  static_assert(NG == 1 || NG == 2, "one or two key groups");
   using G = Geo<D>;
   constexpr int NWG = NW / NG;          // waves per key group
   constexpr int kBM = NWG * kWQ;        // query rows per workgroup
@@ -255,7 +134,7 @@ fwd_bf16_kernel(Params p) {
   if (units % kXcds == 0) unit = (unit % (units / kXcds)) * kXcds + unit / (units / kXcds);
   int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
-  if (PAGED || p.seq_lens != nullptr) b = by_work<NW, PAGED>(p, b, rank_buf);  // heaviest first
+  if (p.seq_lens != nullptr) b = by_work<NW>(p, b, rank_buf);  // heaviest first
   // Inside a unit the group's query heads take consecutive slots for each query tile: heads that
   // read the same K/V rows run side by side (shared L2 lines), and every head's heaviest tiles
   // come before any head's lighter ones.
@@ -265,13 +144,9 @@ fwd_bf16_kernel(Params p) {
   const int H = p.H, N = p.N;
   const int h = g * p.group + hi;
   const int bh = b * H + h;
-  // L: keys of this sequence.  Lq: its valid query rows, which sit at key positions off ..
-  // off + Lq - 1 (a paged prefill chunk is the sequence's newest Lq tokens; otherwise off = 0).
+  // L: valid rows of this sequence (queries and keys alike).
   int L = N;
-  if constexpr (PAGED) L = min(max(p.seq_lens[b], 0), p.max_blocks * kPageRows);
-  else if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
-  const int Lq = PAGED ? min(max(p.q_lens[b], 0), min(L, N)) : L;
-  const int off = PAGED ? L - Lq : 0;
+  if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
 
   const int q0 = qt * kBM;
   const bf16* Qg = p.q + (size_t)bh * N * D;
@@ -280,7 +155,7 @@ fwd_bf16_kernel(Params p) {
   bf16* Og = p.o + (size_t)bh * N * D;
   float* LSEg = p.lse + (size_t)bh * N;
 
-  if (q0 >= Lq) {  // every row of this tile is padding: O = 0, LSE = -inf
+  if (q0 >= L) {  // every row of this tile is padding: O = 0, LSE = -inf
     const int rows = min(kBM, N - q0);
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int i = tid; i < rows * G::CPR; i += kThreads)
@@ -289,63 +164,30 @@ fwd_bf16_kernel(Params p) {
     return;
   }
 
-  const int kv_end = CAUSAL ? min(L, off + q0 + kBM) : L;   // keys this workgroup needs
+  const int kv_end = CAUSAL ? min(L, q0 + kBM) : L;   // keys this workgroup needs
   const int n_kt = (kv_end + kBN - 1) / kBN;
   const int qw0 = q0 + wq * kWQ;
   const int qrow = qw0 + c32;
-  // Tiles this wave needs (fewer than n_kt on the causal diagonal; none for a paged chunk's
-  // wave whose rows are all padding, common when chunks are much shorter than the query tile).
-  const int n_kw = (PAGED && qw0 >= Lq) ? 0
-                 : CAUSAL ? min(n_kt, (min(L, off + qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
+  // Tiles this wave needs (fewer than n_kt on the causal diagonal).
+  const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
   const float sl2 = p.sl2;
   int koff[NI_W], voff[NI_W];
-  if constexpr (PAGED) {
-    tile_offsets_paged<D, NW, false>(koff, wave, lane, p.Hkv * D);
-    tile_offsets_paged<D, NW, true>(voff, wave, lane, p.Hkv * D);
-  } else {
-    tile_offsets<D, NWG, false>(koff, wq, lane);
-    tile_offsets<D, NWG, true>(voff, wq, lane);
-  }
-  // Paged: this wave's rows of every tile lie in one block, block `wblk` of the tile's
-  // kBN / 16; its id for tile j + 1 is fetched one tile ahead (bid_next).  The id is read by a
-  // scalar load (the table is read-only for the kernel's lifetime and the address is uniform):
-  // a vector load would be waited for through the vector-memory counter, which retires in
-  // order, so that wait would also drain the tile loads issued just before it.
-  const int wblk = __builtin_amdgcn_readfirstlane(wave * NI_W * G::RPI / kPageRows);
-  const int* trow = PAGED ? p.table + (size_t)b * p.max_blocks : nullptr;
-  auto block_id = [&](int jt) __attribute__((always_inline)) {
-    const int blk = jt * (kBN / kPageRows) + wblk;
-    return blk * kPageRows < L ? *(const __attribute__((address_space(4))) int*)(trow + blk) : 0;
-  };
-  int bid_next = 0;
-  auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt, int bid) __attribute__((always_inline)) {
-    if constexpr (PAGED) {
-      // A block id outside the pool gets an empty resource: its rows read as zeros.
-      const bool in_pool = (unsigned)bid < (unsigned)p.num_blocks;
-      const int valid = in_pool ? min(max(L - (jt * kBN + wblk * kPageRows), 0), kPageRows) : 0;
-      bid = in_pool ? bid : 0;
-      load_tile_paged<D, NW>(Kd, p.k, bid, g, valid, p.Hkv, koff, wave);
-      load_tile_paged<D, NW>(Vd, p.v, bid, g, valid, p.Hkv, voff, wave);
-    } else {
-      load_tile<D, NWG>(Kd + gofs, Kg, jt * kBN, L, koff, wq);
-      load_tile<D, NWG>(Vd + gofs, Vg, jt * kBN, L, voff, wq);
-    }
+  tile_offsets<D, NWG, false>(koff, wq, lane);
+  tile_offsets<D, NWG, true>(voff, wq, lane);
+  auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt) __attribute__((always_inline)) {
+    load_tile<D, NWG>(Kd + gofs, Kg, jt * kBN, L, koff, wq);
+    load_tile<D, NWG>(Vd + gofs, Vg, jt * kBN, L, voff, wq);
   };
 
   // Issue the first loads before anything else: K_0 and V_0.
-  if constexpr (PAGED) {
-    load_kv(K0, V0, 0, block_id(0));
-    if (1 < n_kt) bid_next = block_id(1);
-  } else if (NG == 1 || grp < n_kt) {
-    load_kv(K0, V0, grp, 0);  // the group's first tile
-  }
+  if (NG == 1 || grp < n_kt) load_kv(K0, V0, grp);  // the group's first tile
 
   // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel; zero for padding
   // rows, so that whatever they hold (NaN included) cannot reach their zero output.
   bf16x8 qf[G::KC];
 #pragma unroll
   for (int c = 0; c < G::KC; ++c) {
-    qf[c] = qrow < Lq ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
+    qf[c] = qrow < L ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
                       : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
   FragAddr<D> fa = frag_addr<D>(lane);
@@ -380,7 +222,7 @@ fwd_bf16_kernel(Params p) {
     constexpr bool M = decltype(masked)::value;
     constexpr int MODE = decltype(mode)::value;
     scores<D>(sA, Kc, fa, qf);
-    if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow + off, hh);
+    if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
     if constexpr (MODE == FAST) {
       // No tile maximum: every probability is at most the lane's share of the tile's row sum,
       // so that sum exceeding 2^kTau is the test that some score outgrew the reference.
@@ -409,7 +251,7 @@ fwd_bf16_kernel(Params p) {
   // need no mask for any wave of the workgroup; the remaining ones (the causal diagonal, the
   // ragged end) are masked.  Iterations are counted for the whole workgroup (n_it, one barrier
   // each) and per wave (n_iw, the iterations whose tile the wave needs).
-  const int n_main = CAUSAL ? min(off + q0, L) / kBN : L / kBN;
+  const int n_main = CAUSAL ? min(q0, L) / kBN : L / kBN;
   const int n_mi = n_main / NG;                  // iterations whose tiles all need no mask
   const int n_it = (n_kt + NG - 1) / NG;
   const int n_iw = (n_kw - grp + NG - 1) / NG;
@@ -419,12 +261,7 @@ fwd_bf16_kernel(Params p) {
     lds_t* const Vc = ODD ? V1 : V0;
     lds_t* const Kn = ODD ? K0 : K1;
     lds_t* const Vn = ODD ? V0 : V1;
-    if ((j + 1) * NG + grp < n_kt) {
-      load_kv(Kn, Vn, (j + 1) * NG + grp, bid_next);
-      if constexpr (PAGED) {
-        if (j + 2 < n_kt) bid_next = block_id(j + 2);
-      }
-    }
+    if ((j + 1) * NG + grp < n_kt) load_kv(Kn, Vn, (j + 1) * NG + grp);
     if (j < n_iw) tile(Kc, Vc, (j * NG + grp) * kBN, masked, mode);
     wait_loads();
     __syncthreads();
@@ -461,12 +298,7 @@ fwd_bf16_kernel(Params p) {
     for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
     m_run = kNegInf;
     l_run = 0.f;
-    if constexpr (PAGED) {
-      load_kv(K0, V0, 0, block_id(0));
-      if (1 < n_kt) bid_next = block_id(1);
-    } else if (NG == 1 || grp < n_kt) {
-      load_kv(K0, V0, grp, 0);
-    }
+    if (NG == 1 || grp < n_kt) load_kv(K0, V0, grp);
     run(std::integral_constant<int, SAFE>{});
   }
 
@@ -514,7 +346,7 @@ fwd_bf16_kernel(Params p) {
 
   // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
   if (qrow < N) {
-    const bool valid = qrow < Lq;
+    const bool valid = qrow < L;
     const float inv = valid ? 1.f / lt : 0.f;
 #pragma unroll
     for (int n = 0; n < G::NB; ++n) {
@@ -539,10 +371,6 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.o = static_cast<bf16*>(a.o);
   p.lse = a.lse;
   p.seq_lens = a.seq_lens;
-  p.table = nullptr;
-  p.q_lens = nullptr;
-  p.max_blocks = 0;
-  p.num_blocks = 0;
   p.H = a.H;
   p.group = a.H / a.Hkv;
   p.Hkv = a.Hkv;
@@ -556,51 +384,19 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   if (wide >= kCUs) {
     p.n_qt = (a.N + 8 * kWQ - 1) / (8 * kWQ);
     p.total = a.B * a.H * p.n_qt;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8, false>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8>), dim3(p.total), dim3(64 * 8), 0, stream, p);
   } else {
     p.n_qt = (a.N + 4 * kWQ - 1) / (4 * kWQ);
     p.total = a.B * a.H * p.n_qt;
     if (p.total <= kCUs)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8, false, 2>), dim3(p.total), dim3(64 * 8), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8, 2>), dim3(p.total), dim3(64 * 8), 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, false>), dim3(p.total), dim3(64 * 4), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), dim3(p.total), dim3(64 * 4), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-// Chunked prefill against the paged cache: the same kernel, K/V tiles gathered through the
-// block table, causal with each sequence's offset L_b - Q_b.
-template <int D>
-hipError_t launch_paged(const PagedPrefillArgs& a, hipStream_t stream) {
-  Params p;
-  p.q = static_cast<const bf16*>(a.q);
-  p.k = static_cast<const bf16*>(a.k_cache);
-  p.v = static_cast<const bf16*>(a.v_cache);
-  p.o = static_cast<bf16*>(a.o);
-  p.lse = a.lse;
-  p.seq_lens = a.seq_lens;
-  p.table = a.block_table;
-  p.q_lens = a.q_lens;
-  p.H = a.Hq;
-  p.group = a.Hq / a.Hkv;
-  p.Hkv = a.Hkv;
-  p.N = a.max_q;
-  p.max_blocks = a.max_blocks;
-  p.num_blocks = a.num_blocks;
-  p.sl2 = a.scale * kLog2e;
-  // Four waves (128 query rows) per workgroup, two workgroups per CU: chunks are often much
-  // shorter than 256 rows, and a wave whose rows are all padding idles its SIMD.
-  p.n_qt = (a.max_q + 4 * kWQ - 1) / (4 * kWQ);
-  p.total = a.S * a.Hq * p.n_qt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4, true>), dim3(p.total), dim3(64 * 4), 0, stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
-  return a.d == 128 ? launch_paged<128>(a, stream) : launch_paged<64>(a, stream);
-}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);

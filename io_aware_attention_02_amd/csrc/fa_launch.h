@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_prefill_plan.h"
 
 namespace fa {
 
@@ -79,8 +80,13 @@ struct PagedPrefillArgs {
   float* lse;  // [S, Hq, max_q]
   int S, max_q, Hq, Hkv, d, max_blocks, num_blocks;
   float scale;
+  void* workspace;  // paged_prefill_workspace_bytes(...) bytes: the plan and the split partials
 };
 
+// The work plan's shape for these sizes (heads per work item, rows per head, resident
+// workgroups) and the workspace it needs; 0 for non-positive sizes.
+plan::Shape paged_prefill_shape(int S, int max_q, int Hq, int Hkv, int max_blocks);
+size_t paged_prefill_workspace_bytes(int S, int max_q, int Hq, int Hkv, int d, int max_blocks);
 hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream);
 
 struct BwdArgs {

@@ -9,6 +9,11 @@
 namespace fa {
 namespace {
 constexpr int kXcdsHost = 8;  // accelerator complex dies of an MI355X
+constexpr int kPrefillResident = 512;  // chunked prefill workgroups: two per CU of an MI355X
+constexpr int kWaveRows = 32;          // query rows per wave of the forward kernels
+
+// Query heads per work item of the chunked prefill: the largest of 4, 2, 1 dividing the group.
+int heads_per_item(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
 }  // namespace
 
 // Floats in one per-row statistics array (D or the base-2 LSE) of the backward's workspace,
@@ -50,6 +55,25 @@ size_t decode_workspace_bytes(int S, int Hq, int d, int max_blocks, int block_si
   if (S <= 0 || Hq <= 0 || d <= 0 || max_blocks <= 0 || block_size <= 0) return 0;
   const size_t slots = (size_t)S * Hq * decode_splits(max_blocks, block_size);
   return slots * ((size_t)d + 2) * sizeof(float);
+}
+
+plan::Shape paged_prefill_shape(int S, int max_q, int Hq, int Hkv, int max_blocks) {
+  const int hp = heads_per_item(Hq / Hkv);
+  plan::Shape s;
+  s.S = S;
+  s.max_q = max_q;
+  s.Hkv = Hkv;
+  s.hgk = Hq / Hkv / hp;
+  s.rph = kWaveRows * 4 / hp;
+  s.max_keys = max_blocks * plan::kPageRows;
+  s.R = kPrefillResident;
+  return s;
+}
+
+size_t paged_prefill_workspace_bytes(int S, int max_q, int Hq, int Hkv, int d, int max_blocks) {
+  if (S <= 0 || max_q <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_blocks <= 0 || Hq % Hkv != 0)
+    return 0;
+  return plan::layout(paged_prefill_shape(S, max_q, Hq, Hkv, max_blocks), d).total;
 }
 
 }  // namespace fa

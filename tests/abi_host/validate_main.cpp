@@ -135,11 +135,20 @@ void unfused() {
 }
 
 void prefill() {
-  auto call = [](int S, int max_q, int Hq, int Hkv, int bs, int mb, int nb, const int32_t* ql) {
+  const size_t need = fa_paged_prefill_workspace_bytes(16, 1024, 32, 8, 128, 2048);
+  auto call = [](int S, int max_q, int Hq, int Hkv, int bs, int mb, int nb, const int32_t* ql,
+                 const void* ws = P(E), size_t wsb = (size_t)-1) {
     return fa_paged_prefill(P(A), P(Bp), P(C), I(Dp), I(Dp + 4), ql, P(E), F(E), S, max_q, Hq, Hkv,
-                            128, bs, mb, nb, 0.1f, nullptr);
+                            128, bs, mb, nb, 0.1f, const_cast<void*>(ws), wsb, nullptr);
   };
-  CHECK("prefill ok", call(16, 1024, 32, 8, 16, 2048, 4096, I(Dp + 8)), FA_OK, "paged_prefill");
+  CHECK("prefill ok", call(16, 1024, 32, 8, 16, 2048, 4096, I(Dp + 8), P(E), need), FA_OK,
+        "paged_prefill");
+  CHECK("prefill short workspace", call(16, 1024, 32, 8, 16, 2048, 4096, I(Dp + 8), P(E), need - 1),
+        FA_ERR_INVALID_ARG, "");
+  CHECK("prefill null workspace", call(16, 1024, 32, 8, 16, 2048, 4096, I(Dp + 8), nullptr),
+        FA_ERR_INVALID_ARG, "");
+  CHECK("prefill misaligned workspace", call(16, 1024, 32, 8, 16, 2048, 4096, I(Dp + 8), P(E + 8)),
+        FA_ERR_INVALID_ARG, "");
   CHECK("prefill null q_lens", call(16, 1024, 32, 8, 16, 2048, 4096, nullptr), FA_ERR_INVALID_ARG, "");
   CHECK("prefill misaligned q_lens", call(16, 1024, 32, 8, 16, 2048, 4096, I(Dp + 2)),
         FA_ERR_INVALID_ARG, "");
@@ -149,8 +158,15 @@ void prefill() {
         FA_ERR_UNSUPPORTED, "");
   CHECK("prefill grid overflow", call(INT_MAX, INT_MAX, INT_MAX, 1, 16, 64, 4096, I(Dp + 8)),
         FA_ERR_UNSUPPORTED, "");
+  CHECK("prefill items overflow", call(1 << 16, 1 << 16, 64, 64, 16, 64, 4096, I(Dp + 8)),
+        FA_ERR_UNSUPPORTED, "");
   CHECK("prefill max_q=INT_MAX", call(1, INT_MAX, 1, 1, 16, 64, 4096, I(Dp + 8)),
         FA_ERR_UNSUPPORTED, "");
+  if (fa_paged_prefill_workspace_bytes(0, 1024, 32, 8, 128, 2048) != 0 ||
+      fa_paged_prefill_workspace_bytes(16, 1024, 32, 5, 128, 2048) != 0) {
+    std::printf("FAIL prefill workspace size of invalid shapes\n");
+    ++failures;
+  }
 }
 
 void decode() {

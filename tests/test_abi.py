@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
                                      "fa_fwd_unfused_workspace_bytes", "fa_paged_decode",
                                      "fa_paged_decode_noalloc",
                                      "fa_paged_decode_workspace_bytes", "fa_paged_prefill",
-                                     "fa_status_str"]
+                                     "fa_paged_prefill_workspace_bytes", "fa_status_str"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -63,6 +63,17 @@ def test_workspace_bytes(lib):
     assert lib.fa_paged_decode_workspace_bytes(1, 1, 64, 1, 16) == 66 * 4
     assert lib.fa_paged_decode_workspace_bytes(0, 32, 128, 2048, 16) == 0
     assert lib.fa_paged_decode_workspace_bytes(4, 32, 128, -1, 16) == 0
+    # Chunked prefill: at most 2048 split partials of 128 rows x (d + 2) floats, plus the plan
+    # (a few ints per sequence and 8 per work item), whatever the lengths.
+    for d in (64, 128):
+        partials = 2048 * 128 * (d + 2) * 4
+        small = lib.fa_paged_prefill_workspace_bytes(1, 16, 8, 8, d, 1)
+        big = lib.fa_paged_prefill_workspace_bytes(64, 1024, 32, 8, d, 2048)
+        assert partials < small < partials + (1 << 20)
+        assert small < big < partials + (1 << 24)
+        assert small % 256 == 0 and big % 256 == 0
+    assert lib.fa_paged_prefill_workspace_bytes(0, 16, 8, 8, 128, 1) == 0
+    assert lib.fa_paged_prefill_workspace_bytes(1, 16, 8, 3, 128, 1) == 0
 
 
 def _fwd(lib, **kw):
@@ -172,11 +183,11 @@ def test_unfused_rejects(lib, kw, status):
 
 def _pre(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, sl=P, ql=P, o=P, lse=P, S=4, Q=64, Hq=32, Hkv=8, d=128, bs=16,
-             M=64, nb=256, scale=0.1, stream=None)
+             M=64, nb=256, scale=0.1, ws=P, wsb=1 << 30, stream=None)
     a.update(kw)
     return lib.fa_paged_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["ql"], a["o"], a["lse"],
                                 a["S"], a["Q"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["M"], a["nb"],
-                                a["scale"], a["stream"])
+                                a["scale"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -184,7 +195,8 @@ def _pre(lib, **kw):
     (dict(sl=None), INVALID), (dict(ql=None), INVALID), (dict(o=None), INVALID),
     (dict(lse=None), INVALID), (dict(S=0), INVALID), (dict(Q=0), INVALID), (dict(M=-1), INVALID),
     (dict(Hq=32, Hkv=5), INVALID), (dict(scale=math.inf), INVALID), (dict(q=P + 8), INVALID),
-    (dict(ql=P + 2), INVALID), (dict(lse=P + 1), INVALID),
+    (dict(ql=P + 2), INVALID), (dict(lse=P + 1), INVALID), (dict(ws=None), INVALID),
+    (dict(ws=P + 8), INVALID), (dict(wsb=1 << 20), INVALID),
     (dict(d=80), UNSUPPORTED), (dict(bs=8), UNSUPPORTED),
     (dict(S=1 << 20, Q=1 << 20, Hq=1 << 8, Hkv=1 << 8), UNSUPPORTED),
     (dict(M=1 << 28), UNSUPPORTED),

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from io_aware_attention_02_amd import fa_paged_decode, fa_paged_prefill
+from io_aware_attention_02_amd import (fa_paged_decode, fa_paged_prefill,
+                                     fa_paged_prefill_workspace_bytes)
 from io_aware_attention_02_amd.inputs import WORKLOADS, paged_prefill_inputs
 from oracle import paged_prefill_ref
 
@@ -188,3 +189,88 @@ def test_paged_prefill_block_ids_outside_the_pool_read_as_zeros():
     ref_table[0, 5] = P
     ref_table[1, 2] = P
     _check(q, kz, vz, ref_table, sl, ql, o, lse, 1 / d ** 0.5)
+
+
+# Split key ranges.  With little total work the split length is its minimum, 16 key tiles (1024
+# keys), so every query block that sees more keys is cut into pieces whose partial results are
+# merged.  The cases cover the head layouts of a work item: 4 query heads per item (group 4 and
+# 8, the latter two head subsets per kv head), 2 (group 2), 1 (groups 1 and 3).
+SPLIT_CASES = [
+    # (S, Hq, Hkv, d, max_q, lens, q_lens)
+    (3, 32, 8, 128, 48, [9000, 4100, 1025], [40, 1, 48]),
+    (2, 16, 8, 128, 100, [6000, 2500], [100, 65]),
+    (2, 12, 4, 64, 70, [5000, 3000], [70, 33]),
+    (2, 8, 8, 128, 40, [7000, 1100], [40, 7]),
+    (1, 64, 8, 128, 20, [12000], [20]),
+    (2, 4, 1, 64, 130, [2100, 16], [130, 16]),
+]
+
+HDR_MERGE, HDR_T = 24, 25  # plan header fields (ints at the start of the workspace)
+
+
+def _run_ws(q, kc, vc, table, lens, qlens, ws):
+    dev = device()
+    o, lse = fa_paged_prefill(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev),
+                              qlens.to(dev), workspace=ws)
+    torch.cuda.synchronize()
+    hdr = ws[:256].view(torch.int32).cpu()
+    return o, lse, int(hdr[HDR_MERGE]), int(hdr[HDR_T])
+
+
+def _workspace(q, table, Hkv):
+    S, Hq, Qmax, d = q.shape
+    n = fa_paged_prefill_workspace_bytes(S, Qmax, Hq, Hkv, d, table.shape[1])
+    return torch.empty(n, dtype=torch.uint8, device=device())
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES,
+                         ids=[f"S{c[0]}Hq{c[1]}Hkv{c[2]}d{c[3]}Q{c[4]}" for c in SPLIT_CASES])
+def test_paged_prefill_split_key_ranges(case):
+    S, Hq, Hkv, d, Q, lens, qls = case
+    say(f"fa_paged_prefill split {case}")
+    q, kc, vc, table, sl, ql = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=321 + Q, seq_lens=lens,
+                                                    q_lens=qls, spare_blocks=2)
+    ws = _workspace(q, table, Hkv)
+    o, lse, n_merge, T = _run_ws(q, kc, vc, table, sl, ql, ws)
+    say(f"  split length {T} tiles, {n_merge} split query blocks")
+    assert T == 16 and n_merge > 0
+    _check(q, kc, vc, table, sl, ql, o, lse, 1 / d ** 0.5)
+
+
+def test_paged_prefill_workspace_reuse_is_deterministic():
+    # Two different calls through one workspace, then the first again: results are bitwise those
+    # of a fresh workspace (the plan rewrites everything it reads; the item order is dynamic but
+    # each item's arithmetic and the merge order are fixed).
+    S, Hq, Hkv, d, Q = 3, 32, 8, 128, 64
+    a = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=331, seq_lens=[8000, 3000, 1500],
+                             q_lens=[64, 9, 40])
+    b = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=332, seq_lens=[700, 5000, 2000],
+                             q_lens=[64, 64, 1])
+    ws = _workspace(a[0], a[3], Hkv)
+    oa1, la1, ma, _ = _run_ws(*a, ws)
+    ob, lb, mb, _ = _run_ws(*b, ws)
+    oa2, la2, _, _ = _run_ws(*a, ws)
+    assert ma > 0 and mb > 0
+    ob_fresh, lb_fresh, _, _ = _run_ws(*b, _workspace(b[0], b[3], Hkv))
+    assert torch.equal(oa1, oa2) and torch.equal(la1, la2)
+    assert torch.equal(ob, ob_fresh) and torch.equal(lb, lb_fresh)
+    _check(*a, oa1, la1, 1 / d ** 0.5)
+    _check(*b, ob, lb, 1 / d ** 0.5)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cap", [128, 48])
+def test_paged_prefill_workload_short_chunks_every_sequence(cap):
+    # The 16 workload contexts (up to 32K keys) with every chunk cut to at most `cap` tokens: the
+    # long key loops are split (split length 117 and 63 tiles) and merged.
+    w = WORKLOADS["paged_prefill"]
+    say(f"fa_paged_prefill workload contexts, chunks <= {cap}, every sequence")
+    q, kc, vc, table, sl, ql = paged_prefill_inputs(w["S"], w["Hq"], w["Hkv"], w["d"], w["max_q"],
+                                                    w["block_size"], w["len_lo"], w["len_hi"],
+                                                    seed=w["seed"])
+    ql = torch.clamp(ql, max=cap)
+    ws = _workspace(q, table, w["Hkv"])
+    o, lse, n_merge, T = _run_ws(q, kc, vc, table, sl, ql, ws)
+    say(f"  split length {T} tiles, {n_merge} split query blocks")
+    assert n_merge > 0
+    _check_rows(q, kc, vc, table, sl, ql, o, lse, 1 / w["d"] ** 0.5, w["seed"] + cap)
