@@ -94,16 +94,44 @@ __device__ __forceinline__ void load_tile_paged(lds_t* dst, const bf16* cache, i
 
 // ---------------------------------------------------------------------------------------------
 // Plan: one workgroup runs the phases of fa_prefill_plan.h, a barrier between phases.
+
+// Exclusive prefix sum of v[0 .. n) in place by one wave (each lane a contiguous chunk, then a
+// scan of the chunk sums across the lanes); returns the total to every lane.
+__device__ long long wave_exclusive_scan(int* v, int n, int lane) {
+  const int per = (n + 63) / 64;
+  const int lo = min(lane * per, n), hi = min(lo + per, n);
+  long long sum = 0;
+  for (int i = lo; i < hi; ++i) sum += v[i];
+  long long inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  long long run = inc - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int x = v[i];
+    v[i] = (int)run;
+    run += x;
+  }
+  return __shfl(inc, 63, 64);
+}
+
+// SMALL (S <= kMaxRanked, chosen by the host): the per-sequence arrays live in LDS, and the
+// compiler sees that they do, so their reads never wait for the item stores in flight.
+template <bool SMALL>
 __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(PrefillParams p) {
   const plan::Shape s = p.shape;
   const int tid = threadIdx.x;
   __shared__ int keys[plan::kMaxRanked];
   // Per-sequence arrays in LDS when the sequences are few enough (the common case), else in the
   // workspace.
-  __shared__ int seq_s[7 * plan::kMaxRanked];
+  __shared__ int seq_s[9 * plan::kMaxRanked];
   __shared__ int pos_s[2 * plan::kXcds * plan::kMaxRanked];
+  __shared__ int hdr_s[plan::kHdrInts];  // the header is built here and copied out at the end
   plan::Bufs w = p.w;
-  if (s.S <= plan::kMaxRanked) {
+  w.hdr = hdr_s;
+  if constexpr (SMALL) {
     w.order = seq_s;
     w.n_items = seq_s + plan::kMaxRanked;
     w.n_zero = seq_s + 2 * plan::kMaxRanked;
@@ -111,6 +139,8 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(PrefillParam
     w.n_entries = seq_s + 4 * plan::kMaxRanked;
     w.slot_base = seq_s + 5 * plan::kMaxRanked;
     w.entry_base = seq_s + 6 * plan::kMaxRanked;
+    w.len_k = seq_s + 7 * plan::kMaxRanked;
+    w.len_q = seq_s + 8 * plan::kMaxRanked;
     w.pos_real = pos_s;
     w.pos_zero = pos_s + plan::kXcds * plan::kMaxRanked;
   }
@@ -119,7 +149,7 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(PrefillParam
   __shared__ int T_s;
 
   // Order: longest key length first.
-  if (s.S <= plan::kMaxRanked) {
+  if constexpr (SMALL) {
     for (int i = tid; i < s.S; i += kPlanThreads) keys[i] = plan::seq_keys(s, p.seq_lens[i]);
     __syncthreads();
     for (int i = tid; i < s.S; i += kPlanThreads) plan::rank_one(s.S, keys, i, w.order);
@@ -145,13 +175,25 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(PrefillParam
   const int T = T_s;
   for (int r = tid; r < s.S; r += kPlanThreads) plan::count_one(s, p.seq_lens, p.q_lens, T, r, w);
   __syncthreads();
-  if (tid <= plan::kXcds) plan::scan_one(s, tid, w, tot);
+  for (int r = tid; r < s.S; r += kPlanThreads) plan::scan_inputs(s, r, w);
+  __syncthreads();
+  // 18 prefix sums (real and zero items of each list, slots, merge entries), one wave each.
+  for (int a = tid >> 6; a < 2 * plan::kXcds + 2; a += kPlanThreads / 64) {
+    int* v = a < plan::kXcds ? w.pos_real + a * s.S
+           : a < 2 * plan::kXcds ? w.pos_zero + (a - plan::kXcds) * s.S
+           : a == 2 * plan::kXcds ? w.slot_base : w.entry_base;
+    const long long total = wave_exclusive_scan(v, s.S, tid & 63);
+    if ((tid & 63) == 0) tot[a] = total;
+  }
   __syncthreads();
   if (tid == 0) plan::header(s, T, tot, w);
   __syncthreads();
-  const long long units = (long long)s.S * plan::units_per_seq(s);
-  for (long long u = tid; u < units; u += kPlanThreads)
-    plan::emit_one(s, p.seq_lens, p.q_lens, T, tot, u, w);
+  // Items: one task per (unit, query block); units of sequences with a split block serially.
+  const int units = s.S * plan::units_per_seq(s);
+  const int tasks = units * plan::blocks_per_unit(s);
+  for (int t = tid; t < tasks; t += kPlanThreads) plan::emit_task(s, tot, t, w);
+  for (int u = tid; u < units; u += kPlanThreads) plan::emit_split(s, T, u, w);
+  for (int i = tid; i < plan::kHdrInts; i += kPlanThreads) p.w.hdr[i] = hdr_s[i];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -398,15 +440,20 @@ prefill_attend_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Merge: one workgroup per split query block (merge entry), two threads per (head, row) pair of
-// the block, each combining D / 2 dimensions of every piece.  All 128 pairs proceed at once, and
-// each thread issues the loads of two pieces before using them, so a block costs about np / 2
-// memory latencies.
+// Merge: two workgroups per split query block (merge entry), four threads per (head, row) pair,
+// each combining D / 4 dimensions.  One pass over the pieces, four at a time with all their
+// loads in flight, rescaling the running sums whenever the reference grows (the online merge of
+// "FlashAttention优化" §3.2.2): a block costs about np / 4 memory latencies.
+constexpr int kMergeTpp = 4;                                // threads per (head, row) pair
+constexpr int kMergePairs = 256 / kMergeTpp;                // pairs per workgroup
+constexpr int kMergeWgs = plan::kSlotPairs / kMergePairs;  // workgroups per merge entry
+constexpr int kMergeAhead = 4;                              // pieces loaded together
 template <int D, int HP>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
   constexpr int RPH = kWQ * 4 / HP;
-  constexpr int DH = D / 2;  // dimensions per thread
-  const int e = blockIdx.x;
+  constexpr int DQ = D / kMergeTpp;  // dimensions per thread
+  constexpr int NV = DQ / 4;
+  const int e = blockIdx.x / kMergeWgs;
   const int* hdr = p.w.hdr;
   if (e >= hdr[plan::kHdrMerge]) return;
   const plan::Shape& s = p.shape;
@@ -420,57 +467,59 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
   const int L = plan::seq_keys(s, p.seq_lens[b]);
   const int Lq = plan::seq_queries(s, L, p.q_lens[b]);
   const int g = hg / s.hgk;
-  const int pair = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int pair = (blockIdx.x % kMergeWgs) * kMergePairs + threadIdx.x / kMergeTpp;
+  const int part = threadIdx.x % kMergeTpp;
   const int hw = pair / RPH;
   const int row = qb * RPH + pair % RPH;
   if (row >= N) return;
   const int h = g * p.group + (hg - g * s.hgk) * HP + hw;
   const size_t bh = (size_t)b * p.Hq + h;
-  bf16* const out = p.o + (bh * N + row) * D + half * DH;
+  bf16* const out = p.o + (bh * N + row) * D + part * DQ;
   if (row >= Lq) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int c = 0; c < DH / 8; ++c) reinterpret_cast<u32x4*>(out)[c] = zero;
-    if (half == 0) p.lse[bh * N + row] = kNegInf;
+    for (int c = 0; c < DQ / 8; ++c) reinterpret_cast<u32x4*>(out)[c] = zero;
+    if (part == 0) p.lse[bh * N + row] = kNegInf;
     return;
   }
   const size_t at0 = (size_t)slot0 * plan::kSlotPairs + pair;
-  auto m_of = [&](int sp) { return p.mpart[at0 + (size_t)sp * plan::kSlotPairs]; };
-  auto l_of = [&](int sp) { return p.lpart[at0 + (size_t)sp * plan::kSlotPairs]; };
-  // M = the largest reference among pieces that saw a key of the row (l > 0).
-  float M = kNegInf;
-  for (int sp = 0; sp < np; sp += 2) {
-    const float m0 = m_of(sp), l0 = l_of(sp);
-    const bool two = sp + 1 < np;
-    const float m1 = two ? m_of(sp + 1) : kNegInf, l1 = two ? l_of(sp + 1) : 0.f;
-    if (l0 > 0.f) M = fmaxf(M, m0);
-    if (l1 > 0.f) M = fmaxf(M, m1);
-  }
-  f32x4 num[DH / 4];
+  f32x4 num[NV];
 #pragma unroll
-  for (int c = 0; c < DH / 4; ++c) num[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int sp = 0; sp < np; sp += 2) {
-    const bool two = sp + 1 < np;
-    const float* o0 = p.opart + (at0 + (size_t)sp * plan::kSlotPairs) * D + half * DH;
-    const float* o1 = two ? o0 + (size_t)plan::kSlotPairs * D : o0;
-    f32x4 x0[DH / 4], x1[DH / 4];
+  for (int c = 0; c < NV; ++c) num[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M = kNegInf, den = 0.f;
+  for (int sp = 0; sp < np; sp += kMergeAhead) {
+    float m[kMergeAhead], l[kMergeAhead];
+    f32x4 x[kMergeAhead][NV];
 #pragma unroll
-    for (int c = 0; c < DH / 4; ++c) {
-      x0[c] = reinterpret_cast<const f32x4*>(o0)[c];
-      x1[c] = reinterpret_cast<const f32x4*>(o1)[c];
+    for (int u = 0; u < kMergeAhead; ++u) {
+      const size_t at = at0 + (size_t)min(sp + u, np - 1) * plan::kSlotPairs;
+      m[u] = p.mpart[at];
+      l[u] = sp + u < np ? p.lpart[at] : 0.f;  // a repeated last piece weighs nothing
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.opart + at * D + part * DQ);
+#pragma unroll
+      for (int c = 0; c < NV; ++c) x[u][c] = src[c];
     }
-    const float l0 = l_of(sp), l1 = two ? l_of(sp + 1) : 0.f;
-    const float w0 = l0 > 0.f ? fast_exp2(m_of(sp) - M) : 0.f;
-    const float w1 = l1 > 0.f ? fast_exp2(m_of(sp + 1) - M) : 0.f;
-    den = fmaf(w0, l0, den);
-    den = fmaf(w1, l1, den);
+    // Pieces that saw no key of the row (l = 0) weigh nothing.
+    float mx = M;
 #pragma unroll
-    for (int c = 0; c < DH / 4; ++c) num[c] = num[c] + w0 * x0[c] + w1 * x1[c];
+    for (int u = 0; u < kMergeAhead; ++u)
+      if (l[u] > 0.f) mx = fmaxf(mx, m[u]);
+    const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
+    den *= a;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) num[c] *= a;
+#pragma unroll
+    for (int u = 0; u < kMergeAhead; ++u) {
+      const float wu = l[u] > 0.f ? fast_exp2(m[u] - mx) : 0.f;
+      den = fmaf(wu, l[u], den);
+#pragma unroll
+      for (int c = 0; c < NV; ++c) num[c] += wu * x[u][c];
+    }
+    M = mx;
   }
   const float inv = 1.f / den;
 #pragma unroll
-  for (int c = 0; c < DH / 8; ++c) {
+  for (int c = 0; c < DQ / 8; ++c) {
     u32x4 wv;
     wv[0] = pack_bf16x2(num[2 * c][0] * inv, num[2 * c][1] * inv);
     wv[1] = pack_bf16x2(num[2 * c][2] * inv, num[2 * c][3] * inv);
@@ -478,20 +527,24 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
     wv[3] = pack_bf16x2(num[2 * c + 1][2] * inv, num[2 * c + 1][3] * inv);
     reinterpret_cast<u32x4*>(out)[c] = wv;
   }
-  if (half == 0) p.lse[bh * N + row] = (M + __log2f(den)) * kLn2;
+  if (part == 0) p.lse[bh * N + row] = (M + __log2f(den)) * kLn2;
 }
 
 template <int D, int HP>
 hipError_t launch_hp(PrefillParams p, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  if (p.shape.S <= plan::kMaxRanked)
+    hipLaunchKernelGGL(prefill_plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prefill_plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_attend_kernel<D, HP>), dim3((unsigned)plan::max_positions(p.shape)),
                      dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_merge_kernel<D, HP>), dim3((unsigned)plan::max_merge_entries(p.shape)),
-                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_merge_kernel<D, HP>),
+                     dim3((unsigned)(plan::max_merge_entries(p.shape) * kMergeWgs)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -113,10 +113,16 @@ FA_PLAN_FN int split_tiles(long long W, int R) {
   return t < kMinPieceTiles ? kMinPieceTiles : (t > (1 << 30) ? (1 << 30) : (int)t);
 }
 
-// XCD of the unit at global rank position u (snake order).
-FA_PLAN_FN int unit_xcd(long long u) {
-  const int r = (int)(u % kXcds);
+// XCD of the unit at global rank position u (snake order; u < 2^31 by the size checks).
+FA_PLAN_FN int unit_xcd(int u) {
+  const int r = u & (kXcds - 1);
   return ((u / kXcds) & 1) ? kXcds - 1 - r : r;
+}
+
+// Units u' < n with unit_xcd(u') == x: each period of 16 holds two (x and 15 - x).
+FA_PLAN_FN int units_below_on_xcd(int n, int x) {
+  const int m = n & (2 * kXcds - 1);
+  return 2 * (n / (2 * kXcds)) + (m > x) + (m > 2 * kXcds - 1 - x);
 }
 
 // Upper bounds that size the workspace (host) and guard every index (device).
@@ -160,28 +166,23 @@ FA_PLAN_FN SeqCounts seq_counts(const Shape& s, int L, int Q, int T) {
 
 // Index of unit j of the sequence at rank r among that sequence's units on XCD x.
 FA_PLAN_FN int unit_rank_on_xcd(int nu, int r, int j) {
-  const long long u0 = (long long)r * nu;
+  const int u0 = r * nu;
   const int x = unit_xcd(u0 + j);
-  int k = 0;
-  for (int jj = 0; jj < j; ++jj) k += unit_xcd(u0 + jj) == x;
-  return k;
+  return units_below_on_xcd(u0 + j, x) - units_below_on_xcd(u0, x);
 }
 
 // Units of the sequence at rank r that land on XCD x.
 FA_PLAN_FN int units_on_xcd(int nu, int r, int x) {
-  const long long u0 = (long long)r * nu;
-  int k = 0;
-  for (int j = 0; j < nu; ++j) k += unit_xcd(u0 + j) == x;
-  return k;
+  return units_below_on_xcd((r + 1) * nu, x) - units_below_on_xcd(r * nu, x);
 }
 
 
 // ---------------------------------------------------------------------------------------------
 // Workspace layout (byte offsets, each region 256-byte aligned).  Per-sequence arrays are
-// indexed by rank; pos_real / pos_zero by rank * 8 + XCD.
+// indexed by rank; pos_real / pos_zero by XCD * S + rank.
 struct Layout {
-  size_t hdr, order, n_items, n_zero, n_slots, n_entries, slot_base, entry_base, pos_real,
-      pos_zero, items, merge, opart, mpart, lpart, total;
+  size_t hdr, order, len_k, len_q, n_items, n_zero, n_slots, n_entries, slot_base, entry_base,
+      pos_real, pos_zero, items, merge, opart, mpart, lpart, total;
 };
 
 FA_PLAN_FN size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -193,6 +194,8 @@ FA_PLAN_FN Layout layout(const Shape& s, int d) {
   const size_t slots = (size_t)max_split_slots(s);
   l.hdr = o;        o = align256(o + sizeof(int) * kHdrInts);
   l.order = o;      o = align256(o + sizeof(int) * S);
+  l.len_k = o;      o = align256(o + sizeof(int) * S);
+  l.len_q = o;      o = align256(o + sizeof(int) * S);
   l.n_items = o;    o = align256(o + sizeof(int) * S);
   l.n_zero = o;     o = align256(o + sizeof(int) * S);
   l.n_slots = o;    o = align256(o + sizeof(int) * S);
@@ -214,6 +217,8 @@ FA_PLAN_FN Layout layout(const Shape& s, int d) {
 struct Bufs {
   int* hdr;
   int* order;
+  int* len_k;  // clamped key length L of the sequence at each rank
+  int* len_q;  // clamped chunk length Q
   int* n_items;
   int* n_zero;
   int* n_slots;
@@ -230,6 +235,8 @@ FA_PLAN_FN Bufs bufs(unsigned char* ws, const Layout& l) {
   Bufs b;
   b.hdr = (int*)(ws + l.hdr);
   b.order = (int*)(ws + l.order);
+  b.len_k = (int*)(ws + l.len_k);
+  b.len_q = (int*)(ws + l.len_q);
   b.n_items = (int*)(ws + l.n_items);
   b.n_zero = (int*)(ws + l.n_zero);
   b.n_slots = (int*)(ws + l.n_slots);
@@ -266,39 +273,49 @@ FA_PLAN_FN void count_one(const Shape& s, const int* seq_lens, const int* q_lens
   const int L = seq_keys(s, seq_lens[b]);
   const int Q = seq_queries(s, L, q_lens[b]);
   const SeqCounts c = seq_counts(s, L, Q, T);
+  w.len_k[r] = L;
+  w.len_q[r] = Q;
   w.n_items[r] = c.items;
   w.n_zero[r] = c.zeros;
   w.n_slots[r] = c.slots;
   w.n_entries[r] = c.entries;
 }
 
-// Phase 3 (lane x = 0..7: the list of XCD x; lane 8: slots and merge entries): running sums over
-// ranks.  tot[x] receives the XCD's real and zero item totals (tot[8 + x]); tot[16], tot[17]
-// the slot and merge entry totals.
-FA_PLAN_FN void scan_one(const Shape& s, int x, const Bufs& w, long long* tot) {
+// Phase 3: running sums over ranks.  Its inputs (per rank r and XCD x): the real and zero
+// items the sequence at rank r puts on list x, and its slots and merge entries; its outputs the
+// exclusive prefix sums of each over r (pos_real[x * S + r], pos_zero[x * S + r], slot_base[r],
+// entry_base[r]) and the totals: tot[x] real and tot[8 + x] zero items of list x, tot[16] slots,
+// tot[17] merge entries.  scan_inputs (per rank) writes the inputs in place; the plan kernel
+// then scans each array in parallel, the host check with scan_serial.
+FA_PLAN_FN void scan_inputs(const Shape& s, int r, const Bufs& w) {
   const int nu = units_per_seq(s);
-  if (x < kXcds) {
-    long long real = 0, zero = 0;
-    for (int r = 0; r < s.S; ++r) {
-      const int k = units_on_xcd(nu, r, x);
-      w.pos_real[r * kXcds + x] = (int)real;
-      w.pos_zero[r * kXcds + x] = (int)zero;
-      real += (long long)k * w.n_items[r];
-      zero += (long long)k * w.n_zero[r];
-    }
-    tot[x] = real;
-    tot[kXcds + x] = zero;
-  } else {
-    long long slots = 0, entries = 0;
-    for (int r = 0; r < s.S; ++r) {
-      w.slot_base[r] = (int)slots;
-      w.entry_base[r] = (int)entries;
-      slots += (long long)nu * w.n_slots[r];
-      entries += (long long)nu * w.n_entries[r];
-    }
-    tot[2 * kXcds] = slots;
-    tot[2 * kXcds + 1] = entries;
+  for (int x = 0; x < kXcds; ++x) {
+    const int k = units_on_xcd(nu, r, x);
+    w.pos_real[x * s.S + r] = k * w.n_items[r];
+    w.pos_zero[x * s.S + r] = k * w.n_zero[r];
   }
+  w.slot_base[r] = nu * w.n_slots[r];
+  w.entry_base[r] = nu * w.n_entries[r];
+}
+
+// Exclusive prefix sum of v[0 .. n) in place; returns the total.
+FA_PLAN_FN long long exclusive_scan_serial(int* v, int n) {
+  long long run = 0;
+  for (int i = 0; i < n; ++i) {
+    const int x = v[i];
+    v[i] = (int)run;
+    run += x;
+  }
+  return run;
+}
+
+FA_PLAN_FN void scan_serial(const Shape& s, const Bufs& w, long long* tot) {
+  for (int x = 0; x < kXcds; ++x) {
+    tot[x] = exclusive_scan_serial(w.pos_real + x * s.S, s.S);
+    tot[kXcds + x] = exclusive_scan_serial(w.pos_zero + x * s.S, s.S);
+  }
+  tot[2 * kXcds] = exclusive_scan_serial(w.slot_base, s.S);
+  tot[2 * kXcds + 1] = exclusive_scan_serial(w.entry_base, s.S);
 }
 
 // Position in the dense array of item k of list x, once the header is written.
@@ -352,36 +369,52 @@ FA_PLAN_FN bool header(const Shape& s, int T, const long long* tot, const Bufs& 
   return ok;
 }
 
-// Phase 5 (per unit u = rank * nu + j): the unit's items, merge entries and slots.
-FA_PLAN_FN void emit_one(const Shape& s, const int* seq_lens, const int* q_lens, int T,
-                         const long long* tot, long long u, const Bufs& w) {
-  if (!w.hdr[kHdrOk]) return;  // a bound was exceeded: the lists are empty
-  const int nu = units_per_seq(s);
-  const int r = (int)(u / nu), j = (int)(u % nu);
-  const int b = w.order[r];
-  const int L = seq_keys(s, seq_lens[b]);
-  const int Q = seq_queries(s, L, q_lens[b]);
+// Phase 5a (per task t = unit * blocks_per_unit + qb, unit = rank * nu + j; t < 2^31 by the
+// size checks): the zero item of a block past the chunk, and the item of a real block of a
+// sequence with no split block.
+FA_PLAN_FN void put_item(const Shape& s, const Bufs& w, int x, long long k_list, int b, int j,
+                         int qb, int t0, int t1, int slot) {
+  const long long at = position(w.hdr, x, k_list);
+  if (at < 0 || at >= max_positions(s)) return;
+  struct alignas(16) Int4 { int v[4]; };
+  Int4* e = reinterpret_cast<Int4*>(w.items + at * kItemInts);
+  e[0] = Int4{{b, j, qb, t0}};
+  e[1] = Int4{{t1, slot, 0, 0}};
+}
+
+FA_PLAN_FN void emit_task(const Shape& s, const long long* tot, int t, const Bufs& w) {
+  if (!w.hdr[kHdrOk]) return;  // a bound was exceeded: the plan is empty
+  const int nq = blocks_per_unit(s), nu = units_per_seq(s);
+  const int u = t / nq;
+  const int qb = t - u * nq;
+  const int r = u / nu, j = u - r * nu;
+  const int L = w.len_k[r], Q = w.len_q[r];
+  const int nb = real_blocks(s, Q);
   const int x = unit_xcd(u);
   const int k = unit_rank_on_xcd(nu, r, j);
-  // List positions of the unit's first real and first zero item.
-  long long it = w.pos_real[r * kXcds + x] + (long long)k * w.n_items[r];
-  long long zt = tot[x] + w.pos_zero[r * kXcds + x] + (long long)k * w.n_zero[r];
+  if (qb >= nb) {
+    const long long zt = tot[x] + w.pos_zero[x * s.S + r] + (long long)k * w.n_zero[r] + (qb - nb);
+    put_item(s, w, x, zt, w.order[r], j, qb, 0, 0, kZeroItem);
+  } else if (w.n_slots[r] == 0) {  // no block of this sequence is split: item qb is block qb
+    const long long it = w.pos_real[x * s.S + r] + (long long)k * w.n_items[r] + qb;
+    put_item(s, w, x, it, w.order[r], j, qb, 0, key_tiles(s, L, Q, qb), kDirect);
+  }
+}
+
+// Phase 5b (per unit u = rank * nu + j, sequences with a split block only): the unit's real
+// items, pieces-major, and the merge entries of its split blocks.
+FA_PLAN_FN void emit_split(const Shape& s, int T, int u, const Bufs& w) {
+  if (!w.hdr[kHdrOk]) return;
+  const int nu = units_per_seq(s);
+  const int r = u / nu, j = u - r * nu;
+  if (w.n_slots[r] == 0) return;
+  const int b = w.order[r];
+  const int L = w.len_k[r], Q = w.len_q[r];
+  const int x = unit_xcd(u);
+  const int k = unit_rank_on_xcd(nu, r, j);
+  long long it = w.pos_real[x * s.S + r] + (long long)k * w.n_items[r];
   const long long slot0 = w.slot_base[r] + (long long)j * w.n_slots[r];
   long long ent = w.entry_base[r] + (long long)j * w.n_entries[r];
-  const long long cap = max_positions(s);
-  auto put = [&](long long k_list, int qb, int t0, int t1, int slot) {
-    const long long at = position(w.hdr, x, k_list);
-    if (at < 0 || at >= cap) return;
-    int* e = w.items + at * kItemInts;
-    e[0] = b;
-    e[1] = j;
-    e[2] = qb;
-    e[3] = t0;
-    e[4] = t1;
-    e[5] = slot;
-    e[6] = 0;
-    e[7] = 0;
-  };
   const int nb = real_blocks(s, Q);
   // Merge entries, in query-block order, and the largest piece count.
   int max_np = 0;
@@ -415,12 +448,12 @@ FA_PLAN_FN void emit_one(const Shape& s, const int* seq_lens, const int* q_lens,
         int t0, t1;
         piece_range(n, np, p, &t0, &t1);
         const long long slot = np > 1 ? sb + p : kDirect;
-        put(it++, qb, t0, t1, slot < max_split_slots(s) ? (int)slot : kBadItem);
+        put_item(s, w, x, it++, b, j, qb, t0, t1,
+                 slot < max_split_slots(s) ? (int)slot : kBadItem);
       }
       if (np > 1) sb += np;
     }
   }
-  for (int qb = nb; qb < blocks_per_unit(s); ++qb) put(zt++, qb, 0, 0, kZeroItem);
 }
 
 }  // namespace plan

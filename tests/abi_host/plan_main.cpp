@@ -74,9 +74,12 @@ Result run_case(const char* name, int S, int max_q, int Hq, int Hkv, int max_blo
   const int T = split_tiles(W * nu, s.R);
   for (int r = 0; r < S; ++r) count_one(s, sl, ql, T, r, w);
   long long tot[2 * kXcds + 2];
-  for (int x = 0; x <= kXcds; ++x) scan_one(s, x, w, tot);
+  for (int r = 0; r < S; ++r) scan_inputs(s, r, w);
+  scan_serial(s, w, tot);
   const bool ok = header(s, T, tot, w);
-  for (long long u = 0; u < (long long)S * nu; ++u) emit_one(s, sl, ql, T, tot, u, w);
+  const int units = S * nu;
+  for (int t = 0; t < units * blocks_per_unit(s); ++t) emit_task(s, tot, t, w);
+  for (int u = 0; u < units; ++u) emit_split(s, T, u, w);
 
   EXPECT(ok, "%s: a total exceeds its bound", name);
   EXPECT(w.hdr[kHdrOk] == 1 && w.hdr[kHdrT] == T, "%s: header", name);
@@ -128,7 +131,7 @@ Result run_case(const char* name, int S, int max_q, int Hq, int Hkv, int max_blo
       if (!fields) continue;
       int r = 0;
       while (r < S && w.order[r] != b) ++r;
-      const bool home = unit_xcd((long long)r * nu + j) == x && k < w.hdr[kHdrCount + x];
+      const bool home = unit_xcd(r * nu + j) == x && k < w.hdr[kHdrCount + x];
       off_xcd += !home;
       const int L = seq_keys(s, sl[b]), Q = seq_queries(s, L, ql[b]);
       if (slot == kZeroItem) {
@@ -210,6 +213,18 @@ Result run_case(const char* name, int S, int max_q, int Hq, int Hkv, int max_blo
 }  // namespace
 
 int main() {
+  // The closed-form XCD counts against a walk over the units.
+  for (int nu = 1; nu <= 40; ++nu)
+    for (int r = 0; r < 24; ++r) {
+      int seen[kXcds] = {0};
+      for (int j = 0; j < nu; ++j) {
+        const int x = unit_xcd(r * nu + j);
+        EXPECT(unit_rank_on_xcd(nu, r, j) == seen[x], "unit rank nu=%d r=%d j=%d", nu, r, j);
+        ++seen[x];
+      }
+      for (int x = 0; x < kXcds; ++x)
+        EXPECT(units_on_xcd(nu, r, x) == seen[x], "units on XCD nu=%d r=%d x=%d", nu, r, x);
+    }
   // The 16-sequence chunked-prefill mix (contexts U[1024, 32768], chunks U[1, 1024]) and the same
   // contexts with chunks cut to 128 and 48 tokens.
   const std::vector<int> L16 = {10154, 19980, 16752, 26921, 29798, 13176, 13126, 9680,

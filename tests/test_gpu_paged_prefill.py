@@ -209,9 +209,12 @@ HDR_MERGE, HDR_T = 24, 25  # plan header fields (ints at the start of the worksp
 
 
 def _run_ws(q, kc, vc, table, lens, qlens, ws):
+    # Outputs start as NaN, so a row the kernels never write fails the comparison.
     dev = device()
-    o, lse = fa_paged_prefill(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev),
-                              qlens.to(dev), workspace=ws)
+    o = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    fa_paged_prefill(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev),
+                     qlens.to(dev), o=o, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     hdr = ws[:256].view(torch.int32).cpu()
     return o, lse, int(hdr[HDR_MERGE]), int(hdr[HDR_T])
