@@ -340,11 +340,14 @@ fwd_fp8_kernel(Params8 p) {
       }
       __builtin_amdgcn_sched_barrier(0);
       // The LDS loads that follow (the next block's K fragments) may be given the registers
-      // that still hold P and V^T for the last of these MFMAs.  The compiler inserts no wait
-      // between an MFMA and a later LDS load into its source registers, and with the 64-deep
-      // FP8 MFMA such a load can land before the operands are consumed (measured: corrupted
-      // output accumulators, gone with a wait here).  Wait out one MFMA (16 passes) first.
-      asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+      // that held P and V^T for the MFMAs just issued.  The compiler orders a later write of an
+      // MFMA's C operand after the MFMA, but not a later load into its A or B operands, and the
+      // 64-deep FP8 MFMA can still be reading those (measured: corrupted accumulators when the
+      // loads follow directly).  A vector read of the last MFMA's result is a read-after-write
+      // on an MFMA result, which the compiler does order: it waits until that MFMA has written
+      // its result, hence read its operands, and MFMAs of one wave complete in issue order.
+      // Adding +0 changes nothing but the sign of a zero.
+      acc[G::NB - 1][15] += 0.f;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
