@@ -277,3 +277,20 @@ def test_paged_prefill_workload_short_chunks_every_sequence(cap):
     say(f"  split length {T} tiles, {n_merge} split query blocks")
     assert n_merge > 0
     _check_rows(q, kc, vc, table, sl, ql, o, lse, 1 / w["d"] ** 0.5, w["seed"] + cap)
+
+
+def test_paged_prefill_more_sequences_than_the_ranked_plan_holds():
+    # 600 sequences: past the 512 the plan ranks, so its per-sequence arrays live in the
+    # workspace instead of LDS and the natural order is kept.  Short contexts and chunks keep the
+    # oracle cheap; every row of every sequence is compared, outputs start as NaN.
+    S, Hq, Hkv, d, Q = 600, 4, 1, 64, 16
+    g = torch.Generator().manual_seed(341)
+    lens = torch.randint(1, 201, (S,), generator=g).tolist()
+    qls = [int(torch.randint(1, min(Q, L) + 1, (1,), generator=g)) for L in lens]
+    qls[0], lens[1], qls[1] = 0, 16, 16  # an empty chunk and a chunk that is the whole sequence
+    say(f"fa_paged_prefill S={S}")
+    q, kc, vc, table, sl, ql = paged_prefill_inputs(S, Hq, Hkv, d, Q, seed=341, seq_lens=lens,
+                                                    q_lens=qls)
+    ws = _workspace(q, table, Hkv)
+    o, lse, _, _ = _run_ws(q, kc, vc, table, sl, ql, ws)
+    _check(q, kc, vc, table, sl, ql, o, lse, 1 / d ** 0.5)
