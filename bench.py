@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,fwd_4k,fwd_gqa,fwd_fp8,bwd,prefill_paged,decode,copy} [--steps K]
+    python bench.py --only {fwd,fwd_causal,fwd_4k,fwd_gqa,fwd_fp8,bwd,prefill_paged,prefill_paged_short,decode,copy} [--steps K]
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -339,7 +339,7 @@ def only(args, torch, dev, wf, wd):
         gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         fn = lambda: fa_bwd(q, k, v, o, lse, dout, gq, gk, gv)  # noqa: E731
         what = "fa_bwd B=1 H=8 N=16384 d=128 bf16 non-causal"
-    elif args.only == "prefill_paged":
+    elif args.only in ("prefill_paged", "prefill_paged_short"):
         from io_aware_attention_02_amd import fa_paged_prefill, fa_paged_prefill_workspace_bytes
         from io_aware_attention_02_amd.inputs import WORKLOADS, paged_prefill_inputs
         w5 = WORKLOADS["paged_prefill"]
@@ -349,8 +349,11 @@ def only(args, torch, dev, wf, wd):
         pws = torch.empty(fa_paged_prefill_workspace_bytes(w5["S"], w5["max_q"], w5["Hq"], w5["Hkv"],
                                                            w5["d"], ptb.shape[1]),
                           dtype=torch.uint8, device=dev)
+        if args.only == "prefill_paged_short":  # the same contexts, chunks cut to 128 tokens
+            pql = torch.clamp(pql, max=128)
         fn = lambda: fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql, workspace=pws)  # noqa: E731
-        what = "fa_paged_prefill 16 seqs, chunks <= 1024 of contexts U[1024,32768], Hq=32 Hkv=8"
+        what = ("fa_paged_prefill 16 seqs, chunks <= " + ("128" if args.only.endswith("short") else "1024")
+                + " of contexts U[1024,32768], Hq=32 Hkv=8")
     elif args.only == "decode":
         dq, kc, vc, table, lens = paged_decode_inputs(wd["S"], wd["Hq"], wd["Hkv"], wd["d"],
                                                       wd["block_size"], wd["len_lo"], wd["len_hi"],
@@ -381,7 +384,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_4k", "fwd_gqa", "fwd_fp8", "bwd",
-                                       "prefill_paged", "decode", "copy"],
+                                       "prefill_paged", "prefill_paged_short", "decode", "copy"],
                     default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
