@@ -77,7 +77,7 @@ class ClockSampler:
     """Samples the GPU's engine (gfx) clock and socket power with amdsmi from a background
     thread while the main thread keeps the GPU busy (it waits in device synchronisations
     meanwhile).  The published peaks assume the maximum clock; the clock held under load is
-    recorded beside the throughput.  The driver's metrics refresh about once a second, so the
+    recorded beside the throughput.  The GPU's metrics refresh about once a second, so the
     window must last a few seconds.  Reports None with the reason if amdsmi cannot read the
     device."""
 
