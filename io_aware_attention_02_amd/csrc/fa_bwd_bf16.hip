@@ -15,12 +15,12 @@
 //                     K and V tiles of 64 keys stream through LDS; S^T = K Q^T and dP^T = V dO^T
 //                     on the matrix cores, dS^T in registers, dQ^T += K^T dS^T with K^T read by
 //                     the transposing LDS read.
-//  * bwd_dkdv_kernel  key-stationary: two waves own each 32 keys (K, V in registers), query tiles
+//  * bwd_dkdv_kernel  key-stationary: the workgroup's 128 K and V rows stay in LDS, query tiles
 //                     of 64 rows of Q and dO (every query head of the kv head's group) stream
-//                     through LDS; one wave forms S = Q K^T, P and dV^T += dO^T P and passes P
-//                     through LDS to its partner, which forms dP = dO V^T, dS and
-//                     dK^T += Q^T dS.  Summing the group's heads inside the kernel keeps
-//                     grouped-query dK/dV free of atomics.
+//                     through LDS; each wave runs S = Q K^T, dP = dO V^T, P, dS,
+//                     dV^T += dO^T P and dK^T += Q^T dS for its 32 keys and 32 of the rows.
+//                     Summing the group's heads inside the kernel keeps grouped-query dK/dV
+//                     free of atomics.
 // Every probability is rebuilt from the stored LSE as exp2(s * scale * log2 e - LSE * log2 e);
 // padding rows get LSE = +inf here so that their probabilities are exactly 0.
 #include "fa_device.h"
@@ -325,23 +325,22 @@ bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (batch, kv head, 128 keys) of 8 waves.  Waves w and w + 4 share a
-// SIMD and own the same 32 keys.  Wave w (the P wave) holds K^T and the dV^T accumulator: it
-// forms S = Q K^T and P for 32 query rows, hands P (fp32, in the accumulator's lane order) to
-// its partner through LDS and adds dV^T += dO^T P.  Wave w + 4 (the dS wave) holds V^T and the
-// dK^T accumulator: it forms dP = dO V^T, takes P from LDS, dS = P o (dP - D) and adds
-// dK^T += Q^T dS.  Each wave thus holds one operand and one accumulator (about 170 registers),
-// two waves fit on a SIMD, and no product is computed twice.
+// dK, dV: one workgroup per (batch, kv head, 128 keys) of 8 waves.  The workgroup's K and V rows
+// stay in LDS for the whole kernel (key-stationary: they are loaded once).  Wave w owns the 32
+// keys of slice s = w & 3 and the rows 32 r .. 32 r + 31 (r = w >> 2) of every 64-row query
+// tile, and runs all four products for that 32 x 32 block itself: S = Q K^T and dP = dO V^T
+// (both operands read from LDS), P = exp2(S - LSE), dS = P o (dP - D), dV^T += dO^T P and
+// dK^T += Q^T dS (the transposed operands by transposing LDS reads).  Nothing passes between
+// waves inside the loop, so the two waves of a SIMD (w and w + 4: the same keys, different
+// rows) run independently and one overlaps the other's vector work with matrix work.  Their
+// partial dK and dV are added once, at the end, through LDS, always wave w + 4's into wave
+// w's: the sum order is fixed and the result deterministic.
 //
-// Query tiles of 64 rows (every query head of the group) are triple-buffered in LDS; each tile
-// is two halves of 32 rows with one workgroup barrier per half, which both publishes P and
-// orders buffer reuse:
-//   P wave:   S(h), P(h) -> LDS | barrier | dV(h), S(h+1), P(h+1) -> LDS | barrier | ...
-//   dS wave:  dP(h)             | barrier | dS(h), dK(h), dP(h+1)        | barrier | ...
-// After the first barrier of tile t every read of tile t-1 is done, so tile t+2 is loaded into
-// its buffer then; it must land before the second barrier of tile t+1.
+// Query tiles of 64 rows (every query head of the group in turn: grouped-query sums need no
+// atomics) are double-buffered in LDS with their LSE and D rows: tile t + 1 loads while tile t
+// is computed, and one workgroup barrier per tile orders the buffer reuse.
 constexpr int kNWkv = 8;
-constexpr int kQBuf = 3;  // query tile buffers
+constexpr int kAheadKV = 2;  // fragment pairs read ahead of their MFMA in the score products
 
 // Row statistics of a query tile (base-2 LSE or D, 64 fp32) straight into LDS, rows at or past
 // the valid length reading 0: with zero Q and dO rows there, P = 1 and dP = D = 0, so such
@@ -359,6 +358,41 @@ __device__ __forceinline__ void load_stats(lds_t* dst, const float* rowbase, int
 #endif
 }
 
+// Hides the value's known bits from the compiler.  Applied once to the per-lane LDS offsets:
+// an offset whose bits the compiler cannot see is added to an array's base address with an
+// add that the fragment read absorbs into its 16-bit immediate offset, so one register serves
+// every array below 64 KB; with the bits known, it ORs each array's base into a register of
+// its own (one set per tile buffer, more than the registers hold).
+__device__ __forceinline__ int hide_bits(int x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
+// One 32 x 32 block of a score product with both operands in LDS: s = A[32 rows] . B[32 rows]
+// over the head dimension (A rows give the output rows, B rows its columns), the fragment pairs
+// read kAheadKV MFMAs ahead.  ao[c], bo[c]: lane offsets of the 16-dim step c in A and B.
+template <int D>
+__device__ __forceinline__ void scores_lds(f32x16& s, const lds_t* a, const int* ao,
+                                           const lds_t* b, const int* bo) {
+  using G = Geo<D>;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  s = f32x16{};
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c)
+    s = mfma32(*reinterpret_cast<const lds_bf16x8*>(a + ao[c]),
+               *reinterpret_cast<const lds_bf16x8*>(b + bo[c]), s);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAheadKV, 0);
+#pragma unroll
+  for (int i = 0; i < G::KC - kAheadKV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadKV, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kNWkv) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdParams p) {
@@ -366,19 +400,26 @@ bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = kNWkv;
   constexpr int kBK = 4 * kWQ;  // keys per workgroup
   constexpr int NI_W = LoadGeo<D, NW>::NI_W;
-  constexpr int kLoadsPerTile = 2 * NI_W + 1;  // per wave: Q and dO tiles, one statistics row
-  __shared__ __attribute__((aligned(1024))) char qs[kQBuf][G::TILE];
-  __shared__ __attribute__((aligned(1024))) char os[kQBuf][G::TILE];
-  __shared__ __attribute__((aligned(16))) float lvec[kQBuf][kBN];  // LSE (base 2) of the rows
-  __shared__ __attribute__((aligned(16))) float dvec[kQBuf][kBN];  // D of the rows
-  // P in fp32, as the dS wave needs it: [half][slice][chunk][rows 0-3 / 8-11 of the chunk][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 pex[2][4][2][2][64];
+  static_assert(kBK == 2 * kBN, "the workgroup's keys are two LDS tiles");
+  // The two query-tile buffers are separate arrays, always named statically (the loop below is
+  // unrolled by two): the compiler then sees that the fragment reads of one buffer cannot alias
+  // the direct loads in flight into the other, and puts no wait for those loads before them.
+  __shared__ __attribute__((aligned(G::TILE))) char q0s[G::TILE];
+  __shared__ __attribute__((aligned(G::TILE))) char q1s[G::TILE];
+  __shared__ __attribute__((aligned(G::TILE))) char o0s[G::TILE];
+  __shared__ __attribute__((aligned(G::TILE))) char o1s[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char ks[2][G::TILE];  // K rows k0 .. k0 + 127
+  __shared__ __attribute__((aligned(1024))) char vs[2][G::TILE];  // V rows
+  __shared__ __attribute__((aligned(16))) float l0s[kBN];  // LSE (base 2) of the rows
+  __shared__ __attribute__((aligned(16))) float l1s[kBN];
+  __shared__ __attribute__((aligned(16))) float d0s[kBN];  // D of the rows
+  __shared__ __attribute__((aligned(16))) float d1s[kBN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, hh = lane >> 5;
-  const int role = __builtin_amdgcn_readfirstlane(wave >> 2);  // 0: P wave, 1: dS wave
   const int slice = wave & 3;
+  const int rh = __builtin_amdgcn_readfirstlane(wave >> 2);  // which 32 rows of each query tile
   int unit, kt;
   unit_of(p, p.n_t, unit, kt);
   const int b = unit / p.Hkv, g = unit - b * p.Hkv;
@@ -400,16 +441,16 @@ bwd_dkdv_kernel(BwdParams p) {
   const int key = kw0 + c32;  // this lane's key column
   const float sl2 = p.sl2;
 
-  // K^T (P wave) or V^T (dS wave) fragments: the B operand of S = Q K^T or dP = dO V^T, zero
-  // past the length.
-  bf16x8 bf[G::KC];
+  int off[NI_W];
+  tile_offsets_b<D, NW>(off, wave, lane);
+  // K and V rows of the workgroup (rows past the length read as zeros), loaded once.
   {
-    const bf16* src = (role == 0 ? p.k : p.v) + (size_t)(b * p.Hkv + g) * N * D;
+    const bf16* Kg = p.k + (size_t)(b * p.Hkv + g) * N * D;
+    const bf16* Vg = p.v + (size_t)(b * p.Hkv + g) * N * D;
 #pragma unroll
-    for (int c = 0; c < G::KC; ++c) {
-      const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      bf[c] = key < L ? *reinterpret_cast<const bf16x8*>(src + (size_t)key * D + c * 16 + hh * 8)
-                      : zero;
+    for (int t = 0; t < 2; ++t) {
+      load_tile<D, NW>((lds_t*)ks[t], Kg, k0 + t * kBN, L, off, wave);
+      load_tile<D, NW>((lds_t*)vs[t], Vg, k0 + t * kBN, L, off, wave);
     }
   }
 
@@ -417,132 +458,158 @@ bwd_dkdv_kernel(BwdParams p) {
   const int qt0 = CAUSAL ? k0 / kBN : 0;
   const int n_q = (L + kBN - 1) / kBN - qt0;
   const int n_it = p.group * n_q;
-  int off[NI_W];
-  tile_offsets_b<D, NW>(off, wave, lane);
-  const FragAddr<D> fa = frag_addr_b<D>(lane);
-  const TrAddr<D> ta = tr_addr_b<D>(lane);
+  // Lane offsets of the fragment reads, the wave's place folded in: row reads of its 32 query
+  // rows (qa) and of its 32 keys (ka), transposing reads of its two 16-row chunks (ta).
+  int qa[G::KC], ka[G::KC];
+  TrAddr<D> ta;
+  {
+    const FragAddr<D> fa = frag_addr_b<D>(lane);
+    const TrAddr<D> t0 = tr_addr_b<D>(lane);
+#pragma unroll
+    for (int c = 0; c < G::KC; ++c) {
+      qa[c] = hide_bits(fa.k[c] + rh * kWQ * G::RB);
+      ka[c] = hide_bits(fa.k[c] + slice * kWQ * G::RB);
+    }
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) {
+      ta.lo[n] = hide_bits(t0.lo[n] + rh * kWQ * G::RB);
+      ta.hi[n] = hide_bits(t0.hi[n] + rh * kWQ * G::RB);
+    }
+  }
   // Odd waves fetch the LSE row, even waves D (redundantly, so that every wave issues the same
-  // number of loads per tile and one vmcnt value waits for a tile).
-  const float* stat_src = (wave & 1) ? p.lse2 : p.dvec;
-  auto issue = [&](int it, int buf) __attribute__((always_inline)) {
+  // number of loads per tile).
+  auto issue = [&](int it, auto parity) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(parity)::value;
     const int hq = g * p.group + it / n_q;
     const int r0 = (qt0 + it % n_q) * kBN;
     const size_t hb = ((size_t)b * p.H + hq) * N;
-    load_tile<D, NW>((lds_t*)qs[buf], p.q + hb * D, r0, L, off, wave);
-    load_tile<D, NW>((lds_t*)os[buf], p.dout + hb * D, r0, L, off, wave);
-    load_stats((wave & 1) ? (lds_t*)lvec[buf] : (lds_t*)dvec[buf], stat_src + hb, r0, L, lane);
+    load_tile<D, NW>((lds_t*)(ODD ? q1s : q0s), p.q + hb * D, r0, L, off, wave);
+    load_tile<D, NW>((lds_t*)(ODD ? o1s : o0s), p.dout + hb * D, r0, L, off, wave);
+    if (wave & 1) load_stats((lds_t*)(ODD ? l1s : l0s), p.lse2 + hb, r0, L, lane);
+    else load_stats((lds_t*)(ODD ? d1s : d0s), p.dvec + hb, r0, L, lane);
   };
 
-  f32x16 acc[G::NB];  // dV^T (P wave) or dK^T (dS wave)
+  f32x16 dk[G::NB], dv[G::NB];  // dK^T and dV^T of the wave's keys, over its rows
 #pragma unroll
-  for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
+  for (int n = 0; n < G::NB; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
 
-  // Half hq of the tile in buffer buf, first stage (before the barrier): the P wave forms S and
-  // P for rows 32 hq .. 32 hq + 31 and publishes P; the dS wave forms dP.
-  auto stage1 = [&](int buf, int q0t, int hq, bf16x8 (&pf)[2], f32x16& sx, auto masked, auto rl) __attribute__((always_inline)) {
+  // This wave's 32 rows of the tile in buffer buf: S and dP, then P and dS for the two 16-row
+  // chunks jj = 2 rh + j2 (a lane holds rows 16 jj + 4 hh + {0..3} and 16 jj + 8 + 4 hh +
+  // {0..3} of its key's column), then dV^T += dO^T P and dK^T += Q^T dS.
+  auto step = [&](auto parity, int q0t, auto masked) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(parity)::value;
     constexpr bool M = decltype(masked)::value;
-    constexpr int R = decltype(rl)::value;
-    const lds_t* rows = (const lds_t*)(R == 0 ? qs[buf] : os[buf]) + hq * 32 * G::RB;
-    scores_block<D>(sx, rows, fa, bf);
-    if constexpr (R == 0) {
-#pragma unroll
-      for (int j2 = 0; j2 < 2; ++j2) {
-        const int jj = 2 * hq + j2;
-        // Rows of chunk jj held by this lane: 16 jj + 4 hh + {0..3} and 16 jj + 8 + 4 hh + {0..3}.
-        const f32x4 la = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 4 * hh]);
-        const f32x4 lb = *reinterpret_cast<const f32x4*>(&lvec[buf][16 * jj + 8 + 4 * hh]);
-        float e[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          float arg = fmaf(sx[8 * j2 + t], sl2, -(t < 4 ? la[t & 3] : lb[t & 3]));
-          if constexpr (M) {
-            const int qr = q0t + 16 * jj + 8 * (t >> 2) + 4 * hh + (t & 3);
-            if (key >= L || (CAUSAL && key > qr)) arg = kNegInf;
-          }
-          e[t] = fast_exp2(arg);
-        }
-        pf[j2] = pack_bf16x8(e);
-        pex[hq][slice][j2][0][lane] = f32x4{e[0], e[1], e[2], e[3]};
-        pex[hq][slice][j2][1][lane] = f32x4{e[4], e[5], e[6], e[7]};
-      }
-    }
-  };
-  // Second stage (after the barrier): dV^T += dO^T P, or dS and dK^T += Q^T dS.
-  auto stage2 = [&](int buf, int hq, const bf16x8 (&pf)[2], const f32x16& sx, auto rl) __attribute__((always_inline)) {
-    constexpr int R = decltype(rl)::value;
+    const lds_t* const Qb = (const lds_t*)(ODD ? q1s : q0s);
+    const lds_t* const Ob = (const lds_t*)(ODD ? o1s : o0s);
+    const float* const lvec = ODD ? l1s : l0s;
+    const float* const dvec = ODD ? d1s : d0s;
+    f32x16 sx, sp;
+    scores_lds<D>(sx, Qb, qa, (const lds_t*)ks, ka);
+    scores_lds<D>(sp, Ob, qa, (const lds_t*)vs, ka);
+    bf16x8 pf[2], df[2];
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
-      const int jj = 2 * hq + j2;
-      bf16x8 opnd;
-      if constexpr (R == 0) {
-        opnd = pf[j2];
-      } else {
-        const f32x4 pa = pex[hq][slice][j2][0][lane];
-        const f32x4 pb = pex[hq][slice][j2][1][lane];
-        const f32x4 da = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 4 * hh]);
-        const f32x4 db = *reinterpret_cast<const f32x4*>(&dvec[buf][16 * jj + 8 + 4 * hh]);
-        float e[8];
+      const int jj = 2 * rh + j2;
+      const f32x4 la = *reinterpret_cast<const f32x4*>(&lvec[16 * jj + 4 * hh]);
+      const f32x4 lb = *reinterpret_cast<const f32x4*>(&lvec[16 * jj + 8 + 4 * hh]);
+      const f32x4 da = *reinterpret_cast<const f32x4*>(&dvec[16 * jj + 4 * hh]);
+      const f32x4 db = *reinterpret_cast<const f32x4*>(&dvec[16 * jj + 8 + 4 * hh]);
+      float e[8], ds[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float pv = t < 4 ? pa[t & 3] : pb[t & 3];
-          e[t] = pv * (sx[8 * j2 + t] - (t < 4 ? da[t & 3] : db[t & 3]));
+      for (int t = 0; t < 8; ++t) {
+        float arg = fmaf(sx[8 * j2 + t], sl2, -(t < 4 ? la[t & 3] : lb[t & 3]));
+        if constexpr (M) {
+          const int qr = q0t + 16 * jj + 8 * (t >> 2) + 4 * hh + (t & 3);
+          if (key >= L || (CAUSAL && key > qr)) arg = kNegInf;
         }
-        opnd = pack_bf16x8(e);
+        e[t] = fast_exp2(arg);
+        ds[t] = e[t] * (sp[8 * j2 + t] - (t < 4 ? da[t & 3] : db[t & 3]));
       }
-      const lds_t* tr = (const lds_t*)(R == 0 ? os[buf] : qs[buf]);
+      pf[j2] = pack_bf16x8(e);
+      df[j2] = pack_bf16x8(ds);
+    }
 #pragma unroll
-      for (int n = 0; n < G::NB; ++n) acc[n] = mfma32(tr_frag<D>(tr, ta, n, jj), opnd, acc[n]);
+    for (int j2 = 0; j2 < 2; ++j2) {  // ta holds the wave's rows: chunk j2 of them is jj
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) dv[n] = mfma32(tr_frag<D>(Ob, ta, n, j2), pf[j2], dv[n]);
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) dk[n] = mfma32(tr_frag<D>(Qb, ta, n, j2), df[j2], dk[n]);
     }
   };
 
-  // Both roles run the same barrier sequence; a wave whose keys all come after a tile's last row
-  // (causal) skips the tile's arithmetic but not its barriers or loads.
-  auto run = [&](auto rl) __attribute__((always_inline)) {
-    issue(0, 0);
-    if (n_it > 1) issue(1, 1);
-    if (n_it > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoadsPerTile));
-    else wait_loads();
-    __syncthreads();
-    int buf = 0;
-    for (int it = 0; it < n_it; ++it) {
-      const int q0t = (qt0 + it % n_q) * kBN;
-      const bool masked = (CAUSAL && q0t < k0 + kBK - 1) || k0 + kBK > L;
-      const bool active = !CAUSAL || q0t + kBN - 1 >= kw0;
-      const int buf2 = buf == 0 ? 2 : buf - 1;  // (buf + 2) % 3
-      bf16x8 pf[2];
-      f32x16 sx;
-      auto half = [&](int hq) __attribute__((always_inline)) {
-        if (active) {
-          if (masked) stage1(buf, q0t, hq, pf, sx, std::true_type{}, rl);
-          else stage1(buf, q0t, hq, pf, sx, std::false_type{}, rl);
-        }
-        if (hq == 1) {  // tile it + 1 (issued a tile ago) must have landed
-          if (it + 2 < n_it) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoadsPerTile));
-          else wait_loads();
-        }
-        __syncthreads();
-        if (hq == 0 && it + 2 < n_it) issue(it + 2, buf2);
-        if (active) stage2(buf, hq, pf, sx, rl);
-      };
-      half(0);
-      half(1);
-      buf = buf == 2 ? 0 : buf + 1;
+  // Tile it in buffer it & 1 (parity static): tile it + 1 loads into the other buffer, which
+  // was last read before the previous barrier.
+  auto iter = [&](int it, auto parity) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(parity)::value;
+    if (it + 1 < n_it) issue(it + 1, std::integral_constant<bool, !ODD>{});
+    const int q0t = (qt0 + it % n_q) * kBN;
+    // A wave whose rows all come before its keys (causal) skips the tile's arithmetic.
+    const bool active = !CAUSAL || q0t + 32 * rh + 31 >= kw0;
+    const bool masked = (CAUSAL && q0t + 32 * rh < kw0 + kWQ - 1) || kw0 + kWQ > L;
+    if (active) {
+      if (masked) step(parity, q0t, std::true_type{});
+      else step(parity, q0t, std::false_type{});
     }
+    wait_loads();  // tile it + 1 has landed
+    __syncthreads();
   };
-  if (role == 0) run(std::integral_constant<int, 0>{});
-  else run(std::integral_constant<int, 1>{});
+  issue(0, std::false_type{});
+  wait_loads();
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    iter(it, std::false_type{});
+    if (it + 1 < n_it) iter(it + 1, std::true_type{});
+  }
+
+  // Wave w + 4 hands its partial sums to wave w through LDS (every tile buffer is free now: the
+  // loop ended with a barrier).  dK^T of slices 0-1 in ks, 2-3 in vs; dV^T of slice 0, 1, 2, 3
+  // in q0s, q1s, o0s, o1s.
+  {
+    constexpr int kAccB = 64 * G::NB * 16 * 4;  // one accumulator of one wave, in bytes
+    static_assert(kAccB == G::TILE, "one wave's accumulator per tile buffer");
+    char* const vslot = slice == 0 ? q0s : slice == 1 ? q1s : slice == 2 ? o0s : o1s;
+    f32x4* const xk = reinterpret_cast<f32x4*>((slice < 2 ? ks[0] : vs[0]) + (slice & 1) * kAccB);
+    f32x4* const xv = reinterpret_cast<f32x4*>(vslot);
+    if (rh == 1) {
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          xk[(n * 4 + r4) * 64 + lane] = f32x4{dk[n][4 * r4], dk[n][4 * r4 + 1], dk[n][4 * r4 + 2], dk[n][4 * r4 + 3]};
+          xv[(n * 4 + r4) * 64 + lane] = f32x4{dv[n][4 * r4], dv[n][4 * r4 + 1], dv[n][4 * r4 + 2], dv[n][4 * r4 + 3]};
+        }
+    }
+    __syncthreads();
+    if (rh == 1) return;
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 a = xk[(n * 4 + r4) * 64 + lane];
+        const f32x4 c = xv[(n * 4 + r4) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          dk[n][4 * r4 + t] += a[t];
+          dv[n][4 * r4 + t] += c[t];
+        }
+      }
+  }
 
   if (key < N) {
-    bf16* out = role == 0 ? dVg : dKg;
-    const float f = role == 0 ? 1.f : p.scale;
 #pragma unroll
     for (int n = 0; n < G::NB; ++n) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[n][4 * r4 + 0] * f, acc[n][4 * r4 + 1] * f);
-        w[1] = pack_bf16x2(acc[n][4 * r4 + 2] * f, acc[n][4 * r4 + 3] * f);
-        *reinterpret_cast<u32x2*>(out + (size_t)key * D + n * 32 + 8 * r4 + 4 * hh) = w;
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dk[n][4 * r4 + 0] * p.scale, dk[n][4 * r4 + 1] * p.scale);
+        wk[1] = pack_bf16x2(dk[n][4 * r4 + 2] * p.scale, dk[n][4 * r4 + 3] * p.scale);
+        wv[0] = pack_bf16x2(dv[n][4 * r4 + 0], dv[n][4 * r4 + 1]);
+        wv[1] = pack_bf16x2(dv[n][4 * r4 + 2], dv[n][4 * r4 + 3]);
+        *reinterpret_cast<u32x2*>(dKg + (size_t)key * D + n * 32 + 8 * r4 + 4 * hh) = wk;
+        *reinterpret_cast<u32x2*>(dVg + (size_t)key * D + n * 32 + 8 * r4 + 4 * hh) = wv;
       }
     }
   }
