@@ -234,7 +234,8 @@ fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void
  * fa_paged_prefill_workspace_bytes -- size in bytes of the device workspace fa_paged_prefill
  * needs for these sizes: the work plan (a few ints per sequence and per work item) and the
  * partial results of split key ranges, whose number is bounded by a constant (2048 slots of 128
- * query rows x (d + 2) floats: 130 MiB at d = 128, 66 MiB at d = 64) whatever the lengths.
+ * query rows, or 1024 of 256 when max_q >= 256, x (d + 2) floats: 130 MiB at d = 128, 66 MiB at
+ * d = 64) whatever the lengths.
  * Returns 0 for non-positive sizes or Hq not a multiple of Hkv.
  */
 size_t fa_paged_prefill_workspace_bytes(int num_seqs, int max_q, int Hq, int Hkv, int d,

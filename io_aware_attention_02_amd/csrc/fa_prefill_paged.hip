@@ -197,16 +197,16 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(PrefillParam
 }
 
 // ---------------------------------------------------------------------------------------------
-// Attend: four waves; wave w serves query head hw = w % HP of the item's head subset and rows
-// rb * 32 .. rb * 32 + 31 (rb = w / HP) of its query block.  All waves share every K/V tile.
-template <int D, int HP>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Attend: NW waves (4: two workgroups per CU; 8: one, every K/V tile shared by all eight); wave
+// w serves query head hw = w % HP of the item's head subset and rows rb * 32 .. rb * 32 + 31
+// (rb = w / HP) of its query block.  All waves share every K/V tile.
+template <int D, int HP, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_attend_kernel(PrefillParams p) {
   using G = Geo<D>;
-  constexpr int NW = 4;
   constexpr int RPH = kWQ * NW / HP;    // query rows per head of an item
   constexpr int NI_W = LoadGeo<D, NW>::NI_W;
-  static_assert(HP * RPH == plan::kSlotPairs, "an item is one partials slot");
+  constexpr int kPairs = kWQ * NW;      // (head, row) pairs of an item: one partials slot
   __shared__ __attribute__((aligned(1024))) char k0s[G::TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[G::TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[G::TILE];
@@ -422,7 +422,7 @@ prefill_attend_kernel(PrefillParams p) {
   } else {
     // A piece: its unnormalised output, reference maximum and row sum, (head, row) pair
     // hw * RPH + rb * 32 + c32 of the slot.  A row that saw none of the piece's keys has l = 0.
-    const size_t pair = (size_t)slot * plan::kSlotPairs + hw * RPH + rb * kWQ + c32;
+    const size_t pair = (size_t)slot * kPairs + hw * RPH + rb * kWQ + c32;
     float* const op = p.opart + pair * D;
 #pragma unroll
     for (int n = 0; n < G::NB; ++n) {
@@ -440,23 +440,23 @@ prefill_attend_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Merge: two workgroups per split query block (merge entry), four threads per (head, row) pair,
-// each combining D / 4 dimensions.  One pass over the pieces, four at a time with all their
+// Merge: pairs / 64 workgroups per split query block (merge entry), four threads per (head, row)
+// pair, each combining D / 4 dimensions.  One pass over the pieces, four at a time with all their
 // loads in flight, rescaling the running sums whenever the reference grows (the online merge of
 // "FlashAttention优化" §3.2.2): a block costs about np / 4 memory latencies.
-constexpr int kMergeTpp = 4;                                // threads per (head, row) pair
-constexpr int kMergePairs = 256 / kMergeTpp;                // pairs per workgroup
-constexpr int kMergeWgs = plan::kSlotPairs / kMergePairs;  // workgroups per merge entry
-constexpr int kMergeAhead = 4;                              // pieces loaded together
+constexpr int kMergeTpp = 4;                  // threads per (head, row) pair
+constexpr int kMergePairs = 256 / kMergeTpp;  // pairs per workgroup
+constexpr int kMergeAhead = 4;                // pieces loaded together
 template <int D, int HP>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
-  constexpr int RPH = kWQ * 4 / HP;
   constexpr int DQ = D / kMergeTpp;  // dimensions per thread
   constexpr int NV = DQ / 4;
-  const int e = blockIdx.x / kMergeWgs;
+  const plan::Shape& s = p.shape;
+  const int RPH = s.rph;                         // = pairs / HP
+  const int wgs = s.pairs / kMergePairs;         // workgroups per merge entry
+  const int e = blockIdx.x / wgs;
   const int* hdr = p.w.hdr;
   if (e >= hdr[plan::kHdrMerge]) return;
-  const plan::Shape& s = p.shape;
   const int* ent = p.w.merge + (size_t)e * plan::kMergeInts;
   const int b = ent[0], hg = ent[1], qb = ent[2], slot0 = ent[3], np = ent[4];
   if (b < 0 || b >= s.S || hg < 0 || hg >= plan::units_per_seq(s) || qb < 0 ||
@@ -467,7 +467,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
   const int L = plan::seq_keys(s, p.seq_lens[b]);
   const int Lq = plan::seq_queries(s, L, p.q_lens[b]);
   const int g = hg / s.hgk;
-  const int pair = (blockIdx.x % kMergeWgs) * kMergePairs + threadIdx.x / kMergeTpp;
+  const int pair = (blockIdx.x % wgs) * kMergePairs + threadIdx.x / kMergeTpp;
   const int part = threadIdx.x % kMergeTpp;
   const int hw = pair / RPH;
   const int row = qb * RPH + pair % RPH;
@@ -482,7 +482,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
     if (part == 0) p.lse[bh * N + row] = kNegInf;
     return;
   }
-  const size_t at0 = (size_t)slot0 * plan::kSlotPairs + pair;
+  const size_t at0 = (size_t)slot0 * s.pairs + pair;
   f32x4 num[NV];
 #pragma unroll
   for (int c = 0; c < NV; ++c) num[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p) {
     f32x4 x[kMergeAhead][NV];
 #pragma unroll
     for (int u = 0; u < kMergeAhead; ++u) {
-      const size_t at = at0 + (size_t)min(sp + u, np - 1) * plan::kSlotPairs;
+      const size_t at = at0 + (size_t)min(sp + u, np - 1) * s.pairs;
       m[u] = p.mpart[at];
       l[u] = sp + u < np ? p.lpart[at] : 0.f;  // a repeated last piece weighs nothing
       const f32x4* src = reinterpret_cast<const f32x4*>(p.opart + at * D + part * DQ);
@@ -538,12 +538,16 @@ hipError_t launch_hp(PrefillParams p, hipStream_t stream) {
     hipLaunchKernelGGL(prefill_plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_attend_kernel<D, HP>), dim3((unsigned)plan::max_positions(p.shape)),
-                     dim3(256), 0, stream, p);
+  if (p.shape.pairs == 8 * kWQ)
+    hipLaunchKernelGGL((prefill_attend_kernel<D, HP, 8>),
+                       dim3((unsigned)plan::max_positions(p.shape)), dim3(64 * 8), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_attend_kernel<D, HP, 4>),
+                       dim3((unsigned)plan::max_positions(p.shape)), dim3(64 * 4), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_merge_kernel<D, HP>),
-                     dim3((unsigned)(plan::max_merge_entries(p.shape) * kMergeWgs)), dim3(256), 0,
+                     dim3((unsigned)(plan::max_merge_entries(p.shape) * (p.shape.pairs / kMergePairs))), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -580,7 +584,7 @@ hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
   p.max_blocks = a.max_blocks;
   p.num_blocks = a.num_blocks;
   p.sl2 = a.scale * kLog2e;
-  const int hp = plan::kSlotPairs / p.shape.rph;  // query heads per work item
+  const int hp = p.shape.pairs / p.shape.rph;  // query heads per work item
   return a.d == 128 ? launch_d<128>(p, hp, stream) : launch_d<64>(p, hp, stream);
 }
 

@@ -9,8 +9,8 @@
 // Vocabulary.  A sequence b has L_b keys in the cache and a chunk of its newest Q_b tokens as
 // queries, at key positions off_b = L_b - Q_b .. L_b - 1 (causal with that offset).  Its
 // Hkv * hgk "units" are (kv head, head subset) pairs: a work item of a unit covers RPH query rows
-// of each of the HP query heads of the subset (4 waves: 32 rows x HP heads x 4 / HP blocks), so
-// the heads that share a kv head read each key/value tile once.  The unit's query blocks
+// of each of the HP query heads of the subset (NW waves of 32 rows: RPH = 32 NW / HP), so the
+// heads that share a kv head read each key/value tile once.  The unit's query blocks
 // qb = 0 .. ceil(Q_b / RPH) - 1 each need the key tiles 0 .. n_kt(b, qb) - 1 (64 keys per tile);
 // blocks past the chunk (up to ceil(max_q / RPH)) are "zero" items that only write the padding
 // output.  A block whose key loop is longer than T tiles is split into np = ceil(n_kt / T)
@@ -55,7 +55,6 @@ constexpr int kXcds = 8;             // accelerator complex dies of an MI355X
 constexpr int kMinPieceTiles = 16;   // shortest split piece (1024 keys)
 constexpr int kItemInts = 8;         // ints per work item
 constexpr int kMergeInts = 8;        // ints per merge entry
-constexpr int kSlotPairs = 128;      // (head, row) pairs of one work item = one partials slot
 constexpr int kPageRows = 16;        // tokens per physical block of the cache
 constexpr int kDirect = -1;          // item slot value: unsplit, writes O and LSE itself
 constexpr int kZeroItem = -2;        // item slot value: padding rows only
@@ -74,9 +73,10 @@ struct Shape {
   int max_q;      // query rows per (sequence, head) in q and o
   int Hkv;        // kv heads
   int hgk;        // head subsets per kv head (group / HP)
-  int rph;        // query rows per head of a work item (32 * 4 / HP)
+  int rph;        // query rows per head of a work item (pairs / HP)
+  int pairs;      // (head, row) pairs of one work item = one partials slot (32 rows per wave)
   int max_keys;   // max_blocks_per_seq * 16: the longest sequence the block table can hold
-  int R;          // resident workgroups of the persistent kernel
+  int R;          // resident workgroups of the attention kernel
 };
 
 FA_PLAN_FN int imin(int a, int b) { return a < b ? a : b; }
@@ -206,9 +206,10 @@ FA_PLAN_FN Layout layout(const Shape& s, int d) {
   l.pos_zero = o;   o = align256(o + sizeof(int) * S * kXcds);
   l.items = o;      o = align256(o + sizeof(int) * kItemInts * (size_t)max_positions(s));
   l.merge = o;      o = align256(o + sizeof(int) * kMergeInts * (size_t)max_merge_entries(s));
-  l.opart = o;      o = align256(o + sizeof(float) * slots * kSlotPairs * (size_t)d);
-  l.mpart = o;      o = align256(o + sizeof(float) * slots * kSlotPairs);
-  l.lpart = o;      o = align256(o + sizeof(float) * slots * kSlotPairs);
+  const size_t pairs = (size_t)s.pairs;
+  l.opart = o;      o = align256(o + sizeof(float) * slots * pairs * (size_t)d);
+  l.mpart = o;      o = align256(o + sizeof(float) * slots * pairs);
+  l.lpart = o;      o = align256(o + sizeof(float) * slots * pairs);
   l.total = o;
   return l;
 }

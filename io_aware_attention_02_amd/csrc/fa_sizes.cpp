@@ -9,8 +9,13 @@
 namespace fa {
 namespace {
 constexpr int kXcdsHost = 8;  // accelerator complex dies of an MI355X
-constexpr int kPrefillResident = 512;  // chunked prefill workgroups: two per CU of an MI355X
-constexpr int kWaveRows = 32;          // query rows per wave of the forward kernels
+constexpr int kCUsHost = 256;   // compute units of an MI355X
+constexpr int kWaveRows = 32;   // query rows per wave of the forward kernels
+// The chunked prefill's attention workgroups have eight waves (one per CU, sharing each key and
+// value tile, as the contiguous forward's 256-row workgroups do) when the chunk tensor holds at
+// least this many rows per head, else four (two per CU): items of 64 rows per head would leave
+// most waves idle on short chunks.
+constexpr int kPrefillWideRows = 256;
 
 // Query heads per work item of the chunked prefill: the largest of 4, 2, 1 dividing the group.
 int heads_per_item(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
@@ -64,9 +69,11 @@ plan::Shape paged_prefill_shape(int S, int max_q, int Hq, int Hkv, int max_block
   s.max_q = max_q;
   s.Hkv = Hkv;
   s.hgk = Hq / Hkv / hp;
-  s.rph = kWaveRows * 4 / hp;
+  const int nw = max_q >= kPrefillWideRows ? 8 : 4;  // waves per attention workgroup
+  s.pairs = kWaveRows * nw;
+  s.rph = s.pairs / hp;
   s.max_keys = max_blocks * plan::kPageRows;
-  s.R = kPrefillResident;
+  s.R = kCUsHost * 8 / nw;  // resident workgroups: one or two per CU
   return s;
 }
 

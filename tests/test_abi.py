@@ -63,8 +63,9 @@ def test_workspace_bytes(lib):
     assert lib.fa_paged_decode_workspace_bytes(1, 1, 64, 1, 16) == 66 * 4
     assert lib.fa_paged_decode_workspace_bytes(0, 32, 128, 2048, 16) == 0
     assert lib.fa_paged_decode_workspace_bytes(4, 32, 128, -1, 16) == 0
-    # Chunked prefill: at most 2048 split partials of 128 rows x (d + 2) floats, plus the plan
-    # (a few ints per sequence and 8 per work item), whatever the lengths.
+    # Chunked prefill: at most 2048 split partials of 128 rows (1024 of 256 rows when max_q >=
+    # 256) x (d + 2) floats, plus the plan (a few ints per sequence and 8 per work item),
+    # whatever the lengths.
     for d in (64, 128):
         partials = 2048 * 128 * (d + 2) * 4
         small = lib.fa_paged_prefill_workspace_bytes(1, 16, 8, 8, d, 1)

@@ -52,6 +52,11 @@ CASES = [
     (3, 4, 1, 128, 300, [0, 300, 77], [0, 300, 0]),
     (2, 16, 4, 128, 640, [640, 4097], [640, 512]),
     (1, 2, 2, 64, 1, [33], [1]),
+    # At least 256 query rows per head: eight-wave work items (64 rows of 4 heads, 128 of 2 or
+    # 256 of 1), with d = 64 and the head layouts of one and two heads per item.
+    (2, 8, 8, 64, 260, [300, 5000], [260, 100]),
+    (2, 12, 6, 128, 256, [256, 3000], [256, 200]),
+    (2, 6, 2, 64, 300, [2000, 310], [290, 300]),
 ]
 
 
@@ -194,7 +199,8 @@ def test_paged_prefill_block_ids_outside_the_pool_read_as_zeros():
 # Split key ranges.  With little total work the split length is its minimum, 16 key tiles (1024
 # keys), so every query block that sees more keys is cut into pieces whose partial results are
 # merged.  The cases cover the head layouts of a work item: 4 query heads per item (group 4 and
-# 8, the latter two head subsets per kv head), 2 (group 2), 1 (groups 1 and 3).
+# 8, the latter two head subsets per kv head), 2 (group 2), 1 (groups 1 and 3), with four-wave
+# items (fewer than 256 query rows per head) and eight-wave ones.
 SPLIT_CASES = [
     # (S, Hq, Hkv, d, max_q, lens, q_lens)
     (3, 32, 8, 128, 48, [9000, 4100, 1025], [40, 1, 48]),
@@ -203,6 +209,10 @@ SPLIT_CASES = [
     (2, 8, 8, 128, 40, [7000, 1100], [40, 7]),
     (1, 64, 8, 128, 20, [12000], [20]),
     (2, 4, 1, 64, 130, [2100, 16], [130, 16]),
+    # Eight-wave items (at least 256 query rows per head): 1, 2 and 4 heads per item.
+    (2, 8, 8, 64, 256, [6000, 2500], [256, 65]),
+    (2, 12, 6, 128, 300, [5000, 3000], [300, 33]),
+    (1, 32, 8, 64, 256, [9000], [256]),
 ]
 
 HDR_MERGE, HDR_T = 24, 25  # plan header fields (ints at the start of the workspace)
