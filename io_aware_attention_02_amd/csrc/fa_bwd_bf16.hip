@@ -331,10 +331,9 @@ bwd_dq_kernel(BwdParams p) {
 // tile, and runs all four products for that 32 x 32 block itself: S = Q K^T and dP = dO V^T
 // (both operands read from LDS), P = exp2(S - LSE), dS = P o (dP - D), dV^T += dO^T P and
 // dK^T += Q^T dS (the transposed operands by transposing LDS reads).  Nothing passes between
-// waves inside the loop, so the two waves of a SIMD (w and w + 4: the same keys, different
-// rows) run independently and one overlaps the other's vector work with matrix work.  Their
-// partial dK and dV are added once, at the end, through LDS, always wave w + 4's into wave
-// w's: the sum order is fixed and the result deterministic.
+// waves inside the loop: the two waves of a SIMD (w and w + 4: the same keys, different rows)
+// meet only at the tile barrier.  Their partial dK and dV are added once, at the end, through
+// LDS, always wave w + 4's into wave w's: the sum order is fixed and the result deterministic.
 //
 // Query tiles of 64 rows (every query head of the group in turn: grouped-query sums need no
 // atomics) are double-buffered in LDS with their LSE and D rows: tile t + 1 loads while tile t
