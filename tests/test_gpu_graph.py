@@ -1,7 +1,8 @@
 """HIP graph capture of the entry points (the C ABI states they are safe to capture).
 
 One graph captures fa_fwd, fa_paged_decode (caller workspace), fa_paged_decode_noalloc (static
-scratch) and fa_paged_prefill (device-side plan, attention and merge).  Between replays the
+scratch) and fa_paged_prefill (device-side plan, attention and merge) twice: with fewer than 256
+query rows per head (four-wave attention workgroups) and with 256 (eight-wave ones).  Between replays the
 program's own eager work rewrites the inputs in place -- new query values, new chunk lengths for
 the prefill (so its plan changes from replay to replay) -- and synchronises; every replay's
 outputs must equal, bitwise, those of eager calls on the same inputs (the kernels are
@@ -47,12 +48,21 @@ def test_graph_replays_match_eager_calls():
     po, pl = torch.empty_like(pq), torch.empty(pq.shape[:3], dtype=torch.float32, device=dev)
     pws = torch.empty(fa_paged_prefill_workspace_bytes(S, Qmax, 32, 8, 128, ptb.shape[1]),
                       dtype=torch.uint8, device=dev)
+    # The same with 256 query rows per head (eight-wave work items).
+    W = 256
+    wq, wkc, wvc, wtb, wsl, wql = paged_prefill_inputs(2, 8, 2, 128, W, seed=505,
+                                                       seq_lens=[4000, 600], q_lens=[256, 130])
+    wq, wkc, wvc, wtb, wsl, wql = (t.to(dev) for t in (wq, wkc, wvc, wtb, wsl, wql))
+    wo, wl = torch.empty_like(wq), torch.empty(wq.shape[:3], dtype=torch.float32, device=dev)
+    wws = torch.empty(fa_paged_prefill_workspace_bytes(2, W, 8, 2, 128, wtb.shape[1]),
+                      dtype=torch.uint8, device=dev)
 
     def captured():
         fa_fwd(q, k, v, o, lse, causal=True, seq_lens=lens)
         fa_paged_decode(dq, kc, vc, table, sl, do, dl, workspace=dws)
         fa_paged_decode_noalloc(dq, kc, vc, table, sl, do2, dl2)
         fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql, po, pl, workspace=pws)
+        fa_paged_prefill(wq, wkc, wvc, wtb, wsl, wql, wo, wl, workspace=wws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -67,23 +77,27 @@ def test_graph_replays_match_eager_calls():
 
     g = torch.Generator(device="cpu").manual_seed(504)
     chunk_sets = [[96, 40, 1, 96], [1, 96, 50, 0], [33, 2, 96, 17], [96, 96, 96, 96]]
+    wide_sets = [[256, 130], [3, 256], [200, 0], [256, 256]]
     for rep, chunks in enumerate(chunk_sets):
         # Eager work between replays: new inputs, written in place.
         q.copy_(torch.randn(q.shape, generator=g).to(torch.bfloat16))
         dq.copy_(torch.randn(dq.shape, generator=g).to(torch.bfloat16))
         pq.copy_(torch.randn(pq.shape, generator=g).to(torch.bfloat16))
         pql.copy_(torch.tensor(chunks, dtype=torch.int32))
+        wq.copy_(torch.randn(wq.shape, generator=g).to(torch.bfloat16))
+        wql.copy_(torch.tensor(wide_sets[rep], dtype=torch.int32))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in (o, lse, do, dl, do2, dl2, po, pl)]
+        got = [t.clone() for t in (o, lse, do, dl, do2, dl2, po, pl, wo, wl)]
         eo, el = fa_fwd(q, k, v, causal=True, seq_lens=lens)
         edo, edl = fa_paged_decode(dq, kc, vc, table, sl)
         eo8, el8 = fa_paged_prefill(pq, pkc, pvc, ptb, psl, pql)
+        ewo, ewl = fa_paged_prefill(wq, wkc, wvc, wtb, wsl, wql)
         torch.cuda.synchronize()
         names = ["fwd O", "fwd LSE", "decode O", "decode LSE", "noalloc O", "noalloc LSE",
-                 "prefill O", "prefill LSE"]
-        want = [eo, el, edo, edl, edo, edl, eo8, el8]
+                 "prefill O", "prefill LSE", "wide prefill O", "wide prefill LSE"]
+        want = [eo, el, edo, edl, edo, edl, eo8, el8, ewo, ewl]
         for name, a, b in zip(names, got, want):
             assert torch.equal(a, b), f"replay {rep} (chunks {chunks}): {name} differs from eager"
-        say(f"  replay {rep}, chunks {chunks}: every output equals the eager call")
+        say(f"  replay {rep}, chunks {chunks} and {wide_sets[rep]}: every output equals the eager call")
