@@ -116,7 +116,8 @@ fwd_bf16_kernel(Params p) {
   __shared__ int rank_buf[2 * kMaxRanked];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in a scalar register
   const int c32 = lane & 31, hh = lane >> 5;
   const int grp = NG > 1 ? __builtin_amdgcn_readfirstlane(wave / NWG) : 0;  // key group
   const int wq = wave - grp * NWG;  // rows wq * 32 .. +31 of the workgroup's query tile

@@ -151,7 +151,8 @@ fwd_fp8_kernel(Params8 p) {
   lds8_t* const V1 = (lds8_t*)v1s;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in a scalar register
   const int c32 = lane & 31, hh = lane >> 5;
 
   // Work unit = (batch, kv head), remapped so its tiles share an XCD (as in the bf16 forward).

@@ -217,7 +217,8 @@ prefill_attend_kernel(PrefillParams p) {
   lds_t* const V1 = (lds_t*)v1s;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in a scalar register
   const int c32 = lane & 31, hh = lane >> 5;
   const int hw = wave % HP, rb = wave / HP;
   const plan::Shape& s = p.shape;
