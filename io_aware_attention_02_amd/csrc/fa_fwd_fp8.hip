@@ -6,12 +6,14 @@
 // v_mfma_f32_32x32x64_f8f6f4 (64-deep contraction, fp32 accumulation): the scores S^T = K Q^T
 // from the codes (the descale factors fold into the softmax scale), and O^T += V^T P^T with the
 // probabilities rounded to e4m3.  The softmax is the online recurrence of "FlashAttention优化"
-// §3.2.1 over blocks of 64 keys with a per-row reference m that moves to a block's maximum only
-// when that maximum exceeds it by more than a factor 2^2: the probabilities exp(s - m) <= 4 are
-// multiplied by 64 before the rounding (at most 256, inside the e4m3 range, and small values
-// stay out of the subnormals); the row sum uses them unrounded, and the output is multiplied
-// by v_scale / sum at the end.  Output and sum are rescaled only when some row's reference
-// moves, which after the first blocks is rare.
+// §3.2.1 over blocks of 64 keys.  The probabilities exp(s - m) relative to a per-row reference m
+// are multiplied by 64 before the rounding (small values stay out of the subnormals); the row
+// sum uses them unrounded, and the output is multiplied by v_scale / sum at the end.  The first
+// pass (FAST) fixes m after the first 128 keys at their maximum + 4 (log2 units), so later
+// blocks need no row maximum and nothing is rescaled; a probability that would not fit e4m3
+// becomes NaN in the conversion and sends the workgroup to the second pass (SAFE), in which m
+// moves to a block's maximum whenever that maximum exceeds it by more than a factor 2^2
+// (probabilities <= 4, 64 p <= 256).
 //
 // CDNA4 mapping:
 //  * A wave owns 32 query rows, an LDS tile is 128 keys (two softmax blocks); workgroups of 8
@@ -51,6 +53,7 @@ constexpr int kWQ8 = 32;               // query rows per wave
 constexpr int kBN8 = 128;              // keys per tile
 constexpr int kPScaleLog2 = 6;         // probabilities are rounded to e4m3 as 64 p
 constexpr float kLagLog2 = 2.f;        // a row's reference moves when outgrown by more than 2^2
+constexpr float kHeadLog2 = 4.f;       // FAST pass: fixed reference 2^4 above the first tile's maximum
 constexpr int kBufFlags8 = 0x00020000; // buffer resource word 3: 32-bit data format, raw
 constexpr int kSchedMfma8 = 0x008;     // instruction-group masks of sched_group_barrier
 constexpr int kSchedDsRead8 = 0x100;
@@ -239,11 +242,25 @@ fwd_fp8_kernel(Params8 p) {
   f32x16 acc[G::NB];
 #pragma unroll
   for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
-  float m_run = kNegInf;  // row reference (log2 units): a maximum, at most 2 below the current one
+  float m_run = kNegInf;  // row reference (log2 units)
   float l_run = 0.f;      // this lane's share of the row sum, times 64
+  float m_seen = kNegInf; // FAST pass: the row maximum over its first tile (log2 units)
 
-  auto tile = [&](const lds8_t* Kc, const lds8_t* Vc, int key0, auto masked) __attribute__((always_inline)) {
+  // The K/V loop runs in one of two passes.
+  //  * SAFE: the lagging reference above on every block; each block needs its row maximum.
+  //  * FAST (first try): the lagging reference on the first tile only, whose exact row maximum
+  //    is kept; then the reference is fixed at that maximum + kHeadLog2 (O and l rescaled once)
+  //    and later blocks compute no maximum.  Every probability is then at most 2^kHeadLog2
+  //    below the row's largest one, and the row's largest is at least 2^-kHeadLog2.  A
+  //    probability above 7.25 (64 p above 464) has no e4m3 code: the conversion returns NaN,
+  //    which the FP8 MFMA carries into every accumulator element of that query, so one NaN test
+  //    per lane after the loop finds it, and the workgroup recomputes in the SAFE pass.  On
+  //    random inputs a row's maximum exceeds its first tile's by at most about 2^5.5 (16K keys),
+  //    so the fallback is rare; inputs holding NaN take it too and give the SAFE result.
+  enum { FIRST = 0, FAST = 1, SAFE = 2 };
+  auto tile = [&](const lds8_t* Kc, const lds8_t* Vc, int key0, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool M = decltype(masked)::value;
+    constexpr int MODE = decltype(mode)::value;
     constexpr int NS = 2 * G::KC;  // score MFMAs of a 64-key block
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
@@ -283,25 +300,31 @@ fwd_fp8_kernel(Params8 p) {
             if (c > thr) s[bl][r] = kNegInf;
           }
       }
-      // Online softmax over this block: the reference moves (and output and sum are rescaled)
-      // only for rows whose maximum outgrew it by more than 2^kLagLog2.
-      float mx = s[0][0];
+      float bias;
+      if constexpr (MODE == FAST) {
+        bias = m_run - (float)kPScaleLog2;  // fixed and finite: p times 64
+      } else {
+        // Online softmax over this block: the reference moves (and output and sum are
+        // rescaled) only for rows whose maximum outgrew it by more than 2^kLagLog2.
+        float mx = s[0][0];
 #pragma unroll
-      for (int bl = 0; bl < 2; ++bl)
+        for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bl][r]);
-      mx = max_xor32(mx);
-      const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
-      const bool grow = mt > m_run + kLagLog2;  // -inf + 2 = -inf: the first key always moves it
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 before any visible key
-        m_run = m_new;
-        l_run *= alpha;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bl][r]);
+        mx = max_xor32(mx);
+        const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
+        if constexpr (MODE == FIRST) m_seen = fmaxf(m_seen, mt);
+        const bool grow = mt > m_run + kLagLog2;  // -inf + 2 = -inf: the first key always moves it
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mt : m_run;
+          const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 before any visible key
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
+          for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
+        }
+        bias = (m_run == kNegInf ? 0.f : m_run) - (float)kPScaleLog2;  // p times 64
       }
-      const float bias = (m_run == kNegInf ? 0.f : m_run) - (float)kPScaleLog2;  // p times 64
       // Probabilities as e4m3 in k-slot order (the B operand of P V), their unrounded sum.
       i32x8 pf;
       float rs = 0.f;
@@ -354,7 +377,7 @@ fwd_fp8_kernel(Params8 p) {
   };
 
   const int n_main = CAUSAL ? min(q0, L) / kBN8 : L / kBN8;
-  auto iter = [&](int j, auto parity, auto masked) __attribute__((always_inline)) {
+  auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(parity)::value;
     lds8_t* const Kc = ODD ? K1 : K0;
     lds8_t* const Vc = ODD ? V1 : V0;
@@ -364,20 +387,56 @@ fwd_fp8_kernel(Params8 p) {
       load_tile8<D, NW>(Kn, Kg, (j + 1) * kBN8, L, koff, wave);
       load_tile8<D, NW>(Vn, Vg, (j + 1) * kBN8, L, voff, wave);
     }
-    if (j < n_kw) tile(Kc, Vc, j * kBN8, masked);
+    if (j < n_kw) tile(Kc, Vc, j * kBN8, masked, mode);
     wait_loads8();
     __syncthreads();
   };
-  wait_loads8();
-  __syncthreads();
-  int j = 0;
-  for (; j + 1 < n_main; j += 2) {
-    iter(j, std::false_type{}, std::false_type{});
-    iter(j + 1, std::true_type{}, std::false_type{});
-  }
-  for (; j < n_kt; ++j) {
-    if (j & 1) iter(j, std::true_type{}, std::true_type{});
-    else iter(j, std::false_type{}, std::true_type{});
+  using even = std::false_type;
+  using odd = std::true_type;
+  using unmasked = std::false_type;
+  using masked = std::true_type;
+  auto run = [&](auto mode) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
+    using first_mode = std::integral_constant<int, MODE == SAFE ? SAFE : FIRST>;
+    // Tile 0 (K_0 and V_0 are loading or loaded): the FAST pass takes its references from it.
+    wait_loads8();
+    __syncthreads();
+    if (0 < n_main) iter(0, even{}, unmasked{}, first_mode{});
+    else iter(0, even{}, masked{}, first_mode{});
+    if constexpr (MODE == FAST) {
+      // Fix the reference: O and l move from the lagging reference to it (a row that saw no
+      // key has O = l = 0; it is padding and takes any finite reference).
+      const float m_fix = (m_seen == kNegInf ? 0.f : m_seen) + kHeadLog2;
+      const float alpha = fast_exp2(m_run - m_fix);
+      m_run = m_fix;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) acc[n] *= alpha;
+    }
+    int j = 1;
+    for (; j + 1 < n_main; j += 2) {
+      iter(j, odd{}, unmasked{}, mode);
+      iter(j + 1, even{}, unmasked{}, mode);
+    }
+    if (j < n_main) {
+      iter(j, odd{}, unmasked{}, mode);
+      ++j;
+    }
+    for (; j < n_kt; ++j) {
+      if (j & 1) iter(j, odd{}, masked{}, mode);
+      else iter(j, even{}, masked{}, mode);
+    }
+  };
+  run(std::integral_constant<int, FAST>{});
+  // A NaN accumulator: some probability overflowed the fixed reference (or an input is NaN).
+  if (__syncthreads_or(acc[0][0] != acc[0][0])) {
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
+    m_run = kNegInf;
+    l_run = 0.f;
+    load_tile8<D, NW>(K0, Kg, 0, L, koff, wave);
+    load_tile8<D, NW>(V0, Vg, 0, L, voff, wave);
+    run(std::integral_constant<int, SAFE>{});
   }
 
   // Epilogue: O = v_scale * acc / l (both carry the factor 64); LSE = ln 2 (m + log2 l - 6).

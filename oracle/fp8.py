@@ -24,6 +24,12 @@ tolerance admits such rounding schemes (and rejects mistakes).  Its reading:
   ``e4m3_round(p_scale * p) / p_scale`` (p_scale = 64 with lag = 2 keeps 64 p <= 256 inside
   the e4m3 range and small probabilities out of the subnormals).  The row sum l uses the
   unrounded p, so the LSE is the exact log-sum-exp of the scaled scores.
+* Optionally (``headroom``) the reference is fixed after the first ``first`` keys: the blocks
+  among them use the lagging reference, then m becomes their maximum + headroom (log2 units),
+  the output and sum are rescaled once, and later blocks keep it.  Every p then lies in
+  (0, 2^headroom] below the row's largest one, which is at least 2^-headroom.  A row in which
+  some ``p_scale * p`` would exceed 464 (no e4m3 code: the conversion gives NaN) is computed
+  with the lagging reference throughout instead.
 
 Because the rounding of p happens relative to the running maximum of each block, the result
 depends on the block size and the lag; the model takes both as arguments, and any choice is one
@@ -81,7 +87,7 @@ def e4m3_round(x):
 
 
 def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False, seq_lens=None,
-                      block=64, p_scale=64.0, lag=2.0, rows=None):
+                      block=64, p_scale=64.0, lag=2.0, rows=None, headroom=None, first=128):
     """FP8 attention forward: (O [B, H, N, d], LSE [B, H, N]) in float64.
 
     q8 [B, H, N, d], k8 and v8 [B, Hkv, N, d]: e4m3 byte codes (uint8).  q_scale, k_scale,
@@ -89,7 +95,9 @@ def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False
     seq_lens, grouped-query heads and padding as for ``attention_ref``.  block: keys per block of
     the online softmax.  p_scale: the factor applied before rounding probabilities to e4m3, or
     None for no rounding.  lag: how far (log2 units) a block's maximum may exceed the row's
-    reference before the reference moves.  rows: None, or a 1-D list of query rows; then only those rows are
+    reference before the reference moves.  headroom, first: None for the lagging reference on
+    every block, else the reference is fixed after the first ``first`` keys (a multiple of
+    ``block``) at their maximum + headroom (log2 units).  rows: None, or a 1-D list of query rows; then only those rows are
     computed (each row's recurrence involves that row alone) and the results are
     [B, H, n_rows, d] and [B, H, n_rows] (rows at or past a sequence's length: O = 0,
     LSE = -inf).
@@ -112,25 +120,42 @@ def attention_fp8_ref(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False
         for h in range(H):
             g = h // group
             ob, lb = _online(q[b, h, sel[valid]], k[b, g, :L], v[b, g, :L], float(scale), counts,
-                             block, p_scale, float(lag) * np.log(2.0))
+                             block, p_scale, float(lag) * np.log(2.0), headroom, first)
             o[b, h, valid] = ob
             lse[b, h, valid] = lb
     return o, lse
 
 
-def _online(qb, kb, vb, scale, counts, block, p_scale, lag):
+def _online(qb, kb, vb, scale, counts, block, p_scale, lag, headroom=None, first=128):
     """Online softmax over key blocks for the rows of one sequence (every row sees >= 1 key).
-    lag is in natural-log units here."""
+    lag is in natural-log units here; headroom in log2 units (None: lagging reference only)."""
     n, L = qb.shape[0], kb.shape[0]
     s = scale * (qb @ kb.T)
     s = np.where(np.arange(L)[None, :] >= counts[:, None], -np.inf, s)
     m = np.full(n, -np.inf)
     l = np.zeros(n)
     acc = np.zeros((n, vb.shape[1]))
+    fixed = None  # rows on the fixed reference: which rows, and the reference
+    if headroom is not None:
+        if first % block:
+            raise ValueError("first must be a multiple of block")
+        seen = s[:, :first].max(axis=1)
+        ref = np.where(seen > -np.inf, seen, 0.0) + float(headroom) * np.log(2.0)
+        # A row whose probabilities stay representable keeps the fixed reference.
+        over = (p_scale is not None) & (s[:, first:].max(axis=1, initial=-np.inf) - ref
+                                         >= np.log(464.0 / (p_scale or 1.0)))
+        fixed = (~over, ref)
     for j0 in range(0, L, block):
         sj = s[:, j0:j0 + block]
         bm = sj.max(axis=1)
-        m_new = np.where(bm > m + lag, bm, m)   # m = -inf: the first visible key sets it
+        if fixed is not None and j0 == first:
+            keep, ref_f = fixed
+            alpha_f = np.where(m > -np.inf, np.exp(np.where(m > -np.inf, m, 0.0) - ref_f), 0.0)
+            acc = np.where(keep[:, None], alpha_f[:, None] * acc, acc)
+            l = np.where(keep, alpha_f * l, l)
+            m = np.where(keep, ref_f, m)
+        lag_rows = np.ones(n, dtype=bool) if fixed is None or j0 < first else ~fixed[0]
+        m_new = np.where(lag_rows & (bm > m + lag), bm, m)   # m = -inf: the first key sets it
         # rows with no visible key so far keep m = -inf and add nothing
         seen = m_new > -np.inf
         ref = np.where(seen, m_new, 0.0)

@@ -7,12 +7,15 @@ V3 part, names FP8 matrix cores only), so the kernel's deviation from that defin
 from the e4m3 format and the way the probabilities enter the P V product:
 
 * Rounding one probability.  The P V operand is e4m3(64 p) / 64 with p = exp(s - m) and m the
-  row's reference, at most the row maximum and at least 2^-2 below the running one, so
-  1 <= max p and p <= 4: 64 p <= 256 never saturates (largest e4m3 value 448).  With 3 mantissa
-  bits, |e4m3(x) - x| <= 2^-4 * 2^floor(log2 x) <= 2^-4 x for x >= 2^-6 (normal numbers) and
-  <= 2^-10 below (subnormal spacing 2^-9).  In units of the normalised probability
-  P_j = p_j / l that is  delta_j = 2^-4 * max(P_j, 2^-12 * P_max),  since 64 p_j >= 2^-6 iff
-  p_j >= 2^-12 and 1 / l <= P_max (because max p >= 1).
+  row's reference.  The kernel's first pass fixes m at the maximum of the row's first 128 keys
+  plus 2^4 and keeps only rows with 64 p <= 464 (a larger value has no e4m3 code and sends the
+  workgroup to the second pass); its second pass keeps m at most the row maximum and at least
+  2^-2 below the running one, so p <= 4.  Either way p <= 7.25 and max p >= 2^-4, and 64 p
+  never saturates beyond rounding 448 < x <= 464 down to 448 (largest e4m3 value).  With 3
+  mantissa bits, |e4m3(x) - x| <= 2^-4 * 2^floor(log2 x) <= 2^-4 x for x >= 2^-6 (normal
+  numbers; also for 448 < x <= 464) and <= 2^-10 below (subnormal spacing 2^-9).  In units of
+  the normalised probability P_j = p_j / l that is  delta_j = 2^-4 * max(P_j, 2^-8 * P_max),
+  since 64 p_j >= 2^-6 iff p_j >= 2^-12 and 1 / l <= 2^4 P_max (because max p >= 2^-4).
 * The rounding errors of different keys are bounded, zero-mean and independent -- the model of
   probabilistic rounding-error analysis (N. J. Higham and T. Mary, "A new approach to
   probabilistic rounding error analysis", SIAM J. Sci. Comput. 41(5), 2019).  Hoeffding's
@@ -42,6 +45,7 @@ the oracle.
 import numpy as np
 
 SCORE_ALLOW = 2.0 ** -7     # allowed error of one score, natural-log units
+SUBNORMAL_FLOOR = 2.0 ** -8  # 2^-12 (64 p subnormal) times 2^4 (max p >= 2^-4), relative to P_max
 HOEFFDING_T = 8.0           # t / sigma of the elementwise bound
 ACC_ALLOW = 2.0 ** -10      # P V accumulation allowance, relative to sum_j P_j |V_j|
 BF16_HALF_ULP = 2.0 ** -8   # output rounding, relative
@@ -57,7 +61,7 @@ def fp8_bounds(p, v, o):
     v = np.asarray(v, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     pmax = p.max(axis=1, keepdims=True)
-    delta = 2.0 ** -4 * np.where(p > 0, np.maximum(p, 2.0 ** -12 * pmax), 0.0)
+    delta = 2.0 ** -4 * np.where(p > 0, np.maximum(p, SUBNORMAL_FLOOR * pmax), 0.0)
     v2 = v * v
     rnd = (delta * delta) @ v2                                  # sum_j (delta_j V_jc)^2
     p2 = p * p

@@ -1,9 +1,10 @@
 """The FP8 tolerance (tests/fp8_bounds.py) separates correct rounding from real mistakes.
 
 CPU only.  A stand-in for the kernel's arithmetic -- ``attention_fp8_ref``, which models one
-rounding scheme (online softmax over 64-key blocks, lagging reference, probabilities rounded as
-e4m3(64 p) / 64), stored to bf16 -- must pass both checks against the exact attention of the
-dequantised inputs; so must other blockings of the same scheme, since the tolerance is derived
+rounding scheme (online softmax over 64-key blocks, a lagging reference or one fixed after the
+first 128 keys, probabilities rounded as e4m3(64 p) / 64), stored to bf16 -- must pass both
+checks against the exact attention of the dequantised inputs; so must other blockings of the
+same scheme, since the tolerance is derived
 from the format and not from one schedule.  Outputs with a plausible mistake (a block of values
 lost, values off by one key, the scores against the wrong key head) must fail.
 """
@@ -20,8 +21,7 @@ from fp8_bounds import check_against_exact
 B, H, HKV, N, D = 1, 4, 2, 1024, 128
 
 
-@pytest.fixture(scope="module")
-def case():
+def case_fn():
     q8, k8, v8, sc, _ = fp8_inputs(B, H, HKV, N, D, seed=31)
     scale = 1 / D ** 0.5
     q = e4m3_decode(q8.numpy()) * sc[0]
@@ -29,6 +29,11 @@ def case():
     v = e4m3_decode(v8.numpy()) * sc[2]
     ro, _, probs = attention_probs_ref(q, k, v, scale)
     return q8, k8, v8, sc, scale, v, ro, probs
+
+
+@pytest.fixture(scope="module")
+def case():
+    return case_fn()
 
 
 def _bf16(x):
@@ -47,8 +52,9 @@ def _check(case, go):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(lag=0.0), dict(block=128, lag=3.0, p_scale=32.0),
-                                dict(block=16)],
-                         ids=["block64_lag2", "block64_lag0", "block128_lag3", "block16"])
+                                dict(block=16), dict(headroom=4.0), dict(headroom=4.0, first=64)],
+                         ids=["block64_lag2", "block64_lag0", "block128_lag3", "block16",
+                              "fixed_ref_h4", "fixed_ref_h4_first64"])
 def test_rounded_probabilities_pass(case, kw):
     worst, agg = _check(case, _model(case, **kw))
     assert worst <= 0.5 and agg <= 0.6, (worst, agg)
@@ -75,3 +81,29 @@ def test_wrong_kv_head_fails(case):
     with pytest.raises(AssertionError):
         worst, agg = _check(case, _bf16(wrong))
         assert agg <= 1.0, agg
+
+
+def test_fixed_reference_falls_back_where_a_late_key_dominates():
+    # Row 700 of head 0 gets a key (650) equal to its own query: its score exceeds the first
+    # 128 keys' maximum by far more than the fixed reference's 2^4 headroom admits (64 p > 464),
+    # so the row is computed with the lagging reference; the other rows keep the fixed one and
+    # still round differently from it.
+    q8, k8, v8, sc, scale, _, _, _ = case_fn()
+    k8 = k8.clone()
+    k8[0, 0, 650] = q8[0, 0, 700]
+    args = (q8.numpy(), k8.numpy(), v8.numpy(), *sc, scale)
+    lagging = attention_fp8_ref(*args)[0]
+    fixed = attention_fp8_ref(*args, headroom=4.0)[0]
+    assert np.array_equal(fixed[0, 0, 700], lagging[0, 0, 700])
+    assert not np.array_equal(fixed[0, 0, 699], lagging[0, 0, 699])
+    exact = attention_fp8_ref(*args, p_scale=None)[0]
+    assert np.abs(fixed - exact).max() < 0.05
+
+
+def test_fixed_reference_and_lse_match_the_lagging_one():
+    # The LSE uses unrounded probabilities: both references give the exact log-sum-exp.
+    q8, k8, v8, sc, scale, _, _, _ = case_fn()
+    args = (q8.numpy(), k8.numpy(), v8.numpy(), *sc, scale)
+    lse_lag = attention_fp8_ref(*args)[1]
+    lse_fix = attention_fp8_ref(*args, headroom=4.0)[1]
+    np.testing.assert_allclose(lse_fix, lse_lag, rtol=0, atol=1e-12)

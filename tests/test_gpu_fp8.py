@@ -13,7 +13,8 @@ Inputs are the N(0,1) prefill tensors quantised per tensor to e4m3 (descale amax
 Shapes cover ragged lengths, both masks, grouped heads and d = 64 / 128; padding lengths with
 the e4m3 NaN code in every padded row; scale 0; the 4K workload in full; the 16K workloads on
 one sampled row of every 128-row query tile of every head (rows drawn per head) plus the tile
-edges.
+edges; keys planted to dominate rows far beyond the first tile's maximum, which send the
+kernel's workgroups from the fixed-reference pass to the lagging one.
 """
 
 import numpy as np
@@ -142,3 +143,44 @@ def test_fp8_workload_16k_every_query_tile(name):
     go, gl = _run(q8, k8, v8, scales, w["causal"])
     assert np.isfinite(go).all() and np.isfinite(gl).all()
     _check_sampled(q8, k8, v8, scales, w["causal"], 1 / w["d"] ** 0.5, go, gl, 128, w["seed"])
+
+
+# The first pass fixes each row's reference 2^4 above the maximum of its first 128 keys; a
+# probability above 7.25 (64 p > 464) has no e4m3 code, and the workgroup recomputes with the
+# lagging reference.  A key equal to a row's own query scores about |q|^2 / sqrt(d), far above
+# the first tile's maximum of random scores.
+HEAD_LOG2, P_LIMIT = 4.0, 464.0 / 64.0
+FALLBACK = [
+    # (B, H, Hkv, N, d, causal, [(head, row, key), ...]); 4-wave (small grid) and 8-wave grids
+    (1, 4, 2, 1031, 128, False, [(0, 700, 650), (1, 1000, 300), (2, 1030, 1030), (3, 100, 900)]),
+    (1, 4, 2, 1031, 128, True, [(0, 700, 650), (1, 1000, 300), (2, 1030, 1030), (3, 256, 200)]),
+    (1, 8, 2, 8192, 128, False, [(0, 5000, 4000), (5, 100, 3000)]),
+    (1, 8, 2, 8192, 128, True, [(0, 5000, 4000), (6, 8191, 130)]),
+]
+
+
+@pytest.mark.parametrize("case", FALLBACK, ids=[f"N{c[3]}H{c[1]}{'c' if c[5] else ''}" for c in FALLBACK])
+def test_fp8_fixed_reference_fallback(case):
+    B, H, Hkv, N, d, causal, plants = case
+    say(f"fa_fwd_fp8 fallback N={N} H={H} causal={causal} plants={plants}")
+    q8, k8, v8, scales, _ = fp8_inputs(B, H, Hkv, N, d, seed=421)
+    group = H // Hkv
+    for h, i, j in plants:
+        k8[0, h // group, j] = q8[0, h, i]
+    q, k, _ = _dequantised(q8, k8, v8, scales)
+    scale = 1 / d ** 0.5
+    sl2 = scale / np.log(2.0)
+    for h, i, j in plants:  # the planted key outgrows what the fixed reference admits
+        s = (q[0, h, i] @ k[0, h // group, : (i + 1 if causal else N)].T) * sl2
+        assert s.max() - s[:128].max() > HEAD_LOG2 + np.log2(P_LIMIT) + 1.0, (h, i, j)
+    go, gl = _run(q8, k8, v8, scales, causal)
+    wg_rows = 256 if B * H * ((N + 255) // 256) >= 256 else 128
+    for h in range(H):
+        rows = set(tile_rows(N, 128, h, 421))
+        for hp, i, _ in plants:  # every row of a planted row's workgroup (all heads of it)
+            if hp == h:
+                rows.update(range(i - i % wg_rows, min(N, i - i % wg_rows + wg_rows)))
+        rows = np.array(sorted(rows))
+        g = h // group
+        _check(q8[:, h:h + 1], k8[:, g:g + 1], v8[:, g:g + 1], scales, causal, None, scale,
+               go[:, h:h + 1, rows], gl[:, h:h + 1, rows], rows=rows)
