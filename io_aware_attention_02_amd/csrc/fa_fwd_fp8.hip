@@ -57,6 +57,7 @@ constexpr float kHeadLog2 = 4.f;       // FAST pass: fixed reference 2^4 above t
 constexpr int kBufFlags8 = 0x00020000; // buffer resource word 3: 32-bit data format, raw
 constexpr int kSchedMfma8 = 0x008;     // instruction-group masks of sched_group_barrier
 constexpr int kSchedDsRead8 = 0x100;
+constexpr int kSchedValu8 = 0x002;
 constexpr int kAhead8 = 2;             // score MFMAs whose K reads are in flight
 constexpr int kAheadV8 = 2;            // P V MFMAs whose V reads are in flight
 
@@ -376,6 +377,118 @@ fwd_fp8_kernel(Params8 p) {
     }
   };
 
+  // FAST tiles that need no mask: the two 64-key blocks overlap inside the wave.  Block 1's
+  // score products run under block 0's softmax and block 0's P V products under block 1's, so
+  // the matrix cores and the vector unit of the wave's SIMD both have work from this wave most
+  // of the time (otherwise each block is products, softmax, products in sequence, and only the
+  // other wave of the SIMD can fill the gaps).  Between the regions a vector read of the last
+  // product issued (x += 0) waits until it has read its operands before the next region's LDS
+  // loads may reuse their registers (the FP8 MFMA operand hazard of the tile below).
+  auto tile_fast = [&](const lds8_t* Kc, const lds8_t* Vc) __attribute__((always_inline)) {
+    constexpr int NS = 2 * G::KC;                     // score MFMAs of a 64-key block
+    constexpr int kValuPerMfma = (120 + NS - 1) / NS;  // a block's softmax over its MFMAs
+    const float bias = m_run - (float)kPScaleLog2;    // fixed and finite: p times 64
+    auto kfrag = [&](int hk, int bl, int c) __attribute__((always_inline)) {
+      const lds8_t* rb = Kc + (64 * hk + 32 * bl) * G::RB;
+      const u32x4 a0 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][0]);
+      const u32x4 a1 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][1]);
+      return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    };
+    auto vfrag = [&](int hk, int n) __attribute__((always_inline)) {
+      i32x8 vf;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(Vc + vaddr[n] + (64 * hk + 16 * q) * G::RB));
+        vf[2 * q] = r2[0];
+        vf[2 * q + 1] = r2[1];
+      }
+      return vf;
+    };
+    auto score_mfmas = [&](f32x16 (&sc)[2], int hk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bl = 0; bl < 2; ++bl) {
+        sc[bl] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < G::KC; ++c) sc[bl] = mfma8(kfrag(hk, bl, c), qf[c], sc[bl]);
+      }
+    };
+    // Probabilities as e4m3 in k-slot order (the B operand of P V), their unrounded sum.
+    auto probs = [&](const f32x16 (&sc)[2], i32x8& pf) __attribute__((always_inline)) {
+      float rs = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) e[t] = fast_exp2(fmaf(sc[w >> 2][4 * (w & 3) + t], sl2, -bias));
+        rs += (e[0] + e[1]) + (e[2] + e[3]);
+        pf[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+      }
+      return rs;
+    };
+    auto pv_mfmas = [&](const i32x8& pf, int hk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) acc[n] = mfma8(vfrag(hk, n), pf, acc[n]);
+    };
+    f32x16 s0[2], s1[2];
+    i32x8 pf0, pf1;
+    // S(0): the score products of keys 0..63 (K reads kAhead8 MFMAs ahead).
+    __builtin_amdgcn_sched_barrier(0);
+    score_mfmas(s0, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2 * kAhead8, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma8, 1, 0);
+      if (i + kAhead8 < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s0[1][15] += 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    // A: S(1) under the softmax of block 0.
+    score_mfmas(s1, 1);
+    float rs0 = probs(s0, pf0);
+    // The sums feed l only at the tile's end; without this use the adds (and the exponentials
+    // they read) would be moved there, after every product of the tile.
+    asm volatile("" : "+v"(rs0));
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2 * kAhead8, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma8, 1, 0);
+      if (i + kAhead8 < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu8, kValuPerMfma, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s1[1][15] += 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    // B: P V of block 0 under the softmax of block 1.
+    pv_mfmas(pf0, 0);
+    float rs1 = probs(s1, pf1);
+    asm volatile("" : "+v"(rs1));
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4 * kAheadV8, 0);
+#pragma unroll
+    for (int i = 0; i < G::NB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma8, 1, 0);
+      if (i + kAheadV8 < G::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu8, (120 + G::NB - 1) / G::NB, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    acc[G::NB - 1][15] += 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    // C: P V of block 1.
+    pv_mfmas(pf1, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4 * kAheadV8, 0);
+#pragma unroll
+    for (int i = 0; i < G::NB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma8, 1, 0);
+      if (i + kAheadV8 < G::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    acc[G::NB - 1][15] += 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    l_run += rs0 + rs1;
+  };
+
   const int n_main = CAUSAL ? min(q0, L) / kBN8 : L / kBN8;
   auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(parity)::value;
@@ -387,7 +500,10 @@ fwd_fp8_kernel(Params8 p) {
       load_tile8<D, NW>(Kn, Kg, (j + 1) * kBN8, L, koff, wave);
       load_tile8<D, NW>(Vn, Vg, (j + 1) * kBN8, L, voff, wave);
     }
-    if (j < n_kw) tile(Kc, Vc, j * kBN8, masked, mode);
+    if (j < n_kw) {
+      if constexpr (decltype(mode)::value == FAST && !decltype(masked)::value) tile_fast(Kc, Vc);
+      else tile(Kc, Vc, j * kBN8, masked, mode);
+    }
     wait_loads8();
     __syncthreads();
   };
