@@ -521,6 +521,13 @@ def main():
         },
     }
 
+    # The part holds its clock below the published peak's under this load (power limit); the
+    # same rate as a fraction of the peak scaled to the median clock it held.
+    ec = out["engine_clock"]
+    if ec.get("mhz_median"):
+        ec["frac_of_peak_at_median_clock"] = round(
+            tflops / (acc.MI355X_BF16_DENSE_TFLOPS * ec["mhz_median"] / acc.MI355X_PEAK_MHZ), 4)
+
     if not args.no_extras:
         extras = {}
         wc = WORKLOADS["prefill_16k_causal"]

@@ -32,11 +32,13 @@ __all__ = [
     "MI355X_BF16_DENSE_TFLOPS",
     "MI355X_FP8_DENSE_TFLOPS",
     "MI355X_HBM_GBPS",
+    "MI355X_PEAK_MHZ",
 ]
 
 MI355X_BF16_DENSE_TFLOPS = 2500.0   # published dense bf16 matrix peak
 MI355X_FP8_DENSE_TFLOPS = 5000.0    # published dense fp8 matrix peak
 MI355X_HBM_GBPS = 8000.0            # published HBM3E peak
+MI355X_PEAK_MHZ = 2400.0            # engine clock the published matrix peaks assume
 
 
 def attention_flops(B, H, N, d, causal=False, seq_lens=None):
