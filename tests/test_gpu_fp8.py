@@ -156,10 +156,13 @@ FALLBACK = [
     (1, 4, 2, 1031, 128, True, [(0, 700, 650), (1, 1000, 300), (2, 1030, 1030), (3, 256, 200)]),
     (1, 8, 2, 8192, 128, False, [(0, 5000, 4000), (5, 100, 3000)]),
     (1, 8, 2, 8192, 128, True, [(0, 5000, 4000), (6, 8191, 130)]),
+    (1, 4, 2, 1031, 64, False, [(0, 150, 129), (1, 1030, 200), (2, 300, 129), (3, 500, 250)]),
+    (1, 4, 2, 1031, 64, True, [(0, 150, 129), (1, 1030, 200), (2, 300, 129), (3, 500, 250)]),
 ]
 
 
-@pytest.mark.parametrize("case", FALLBACK, ids=[f"N{c[3]}H{c[1]}{'c' if c[5] else ''}" for c in FALLBACK])
+@pytest.mark.parametrize("case", FALLBACK,
+                         ids=[f"N{c[3]}H{c[1]}d{c[4]}{'c' if c[5] else ''}" for c in FALLBACK])
 def test_fp8_fixed_reference_fallback(case):
     B, H, Hkv, N, d, causal, plants = case
     say(f"fa_fwd_fp8 fallback N={N} H={H} causal={causal} plants={plants}")
