@@ -259,28 +259,73 @@ fwd_fp8_kernel(Params8 p) {
   //    random inputs a row's maximum exceeds its first tile's by at most about 2^5.5 (16K keys),
   //    so the fallback is rare; inputs holding NaN take it too and give the SAFE result.
   enum { FIRST = 0, FAST = 1, SAFE = 2 };
+  constexpr int NS = 2 * G::KC;  // score MFMAs of a 64-key block
+  // K fragment (A operand) of 32-key block bl of 64-key block hk, 64-deep step c: two 16-byte
+  // row reads.
+  auto kfrag = [&](const lds8_t* Kc, int hk, int bl, int c) __attribute__((always_inline)) {
+    const lds8_t* rb = Kc + (64 * hk + 32 * bl) * G::RB;
+    const u32x4 a0 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][0]);
+    const u32x4 a1 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][1]);
+    return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  };
+  // V^T fragment (A operand of P V) of output block n and 64-key block hk: four transposing
+  // reads of the keys 64 hk + 16 q ...
+  auto vfrag = [&](const lds8_t* Vc, int hk, int n) __attribute__((always_inline)) {
+    i32x8 vf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_i32x2*)(Vc + vaddr[n] + (64 * hk + 16 * q) * G::RB));
+      vf[2 * q] = r2[0];
+      vf[2 * q + 1] = r2[1];
+    }
+    return vf;
+  };
+  // Scores of keys 64 hk .. 64 hk + 63 (two 32-key blocks).
+  auto score_mfmas = [&](f32x16 (&sc)[2], const lds8_t* Kc, int hk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bl = 0; bl < 2; ++bl) {
+      sc[bl] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < G::KC; ++c) sc[bl] = mfma8(kfrag(Kc, hk, bl, c), qf[c], sc[bl]);
+    }
+  };
+  // Probabilities exp2(s sl2 - bias) as e4m3 in k-slot order (the B operand of P V); returns
+  // their unrounded sum.  On masked tiles a masked score (-inf) gives exactly 0, also when the
+  // scale is 0 (where -inf * 0 would be NaN).
+  auto probs = [&](const f32x16 (&sc)[2], float bias, i32x8& pf, auto masked) __attribute__((always_inline)) {
+    constexpr bool M = decltype(masked)::value;
+    float rs = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float e[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float x = sc[w >> 2][4 * (w & 3) + t];
+        float arg = fmaf(x, sl2, -bias);
+        if (M && x == kNegInf) arg = kNegInf;
+        e[t] = fast_exp2(arg);
+      }
+      rs += (e[0] + e[1]) + (e[2] + e[3]);
+      pf[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+    }
+    return rs;
+  };
+  auto pv_mfmas = [&](const i32x8& pf, const lds8_t* Vc, int hk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < G::NB; ++n) acc[n] = mfma8(vfrag(Vc, hk, n), pf, acc[n]);
+  };
+
   auto tile = [&](const lds8_t* Kc, const lds8_t* Vc, int key0, auto masked, auto mode) __attribute__((always_inline)) {
     constexpr bool M = decltype(masked)::value;
     constexpr int MODE = decltype(mode)::value;
-    constexpr int NS = 2 * G::KC;  // score MFMAs of a 64-key block
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
       f32x16 s[2];
       // Scores of keys 64 hk .. 64 hk + 63: two 16-byte K reads per MFMA, kAhead8 MFMAs ahead.
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bl = 0; bl < 2; ++bl) {
-        s[bl] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < G::KC; ++c) {
-          const lds8_t* rb = Kc + (64 * hk + 32 * bl) * G::RB;
-          const u32x4 a0 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][0]);
-          const u32x4 a1 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][1]);
-          const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          s[bl] = mfma8(af, qf[c], s[bl]);
-        }
-      }
+      score_mfmas(s, Kc, hk);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2 * kAhead8, 0);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -326,37 +371,11 @@ fwd_fp8_kernel(Params8 p) {
         }
         bias = (m_run == kNegInf ? 0.f : m_run) - (float)kPScaleLog2;  // p times 64
       }
-      // Probabilities as e4m3 in k-slot order (the B operand of P V), their unrounded sum.
       i32x8 pf;
-      float rs = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        float e[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float x = s[w >> 2][4 * (w & 3) + t];
-          float arg = fmaf(x, sl2, -bias);
-          if (M && x == kNegInf) arg = kNegInf;  // exactly 0, also when the scale is 0
-          e[t] = fast_exp2(arg);
-        }
-        rs += (e[0] + e[1]) + (e[2] + e[3]);
-        pf[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
-      }
-      l_run += rs;
+      l_run += probs(s, bias, pf, masked);
       // P V: per output block four transposing V reads (keys 64 hk + 16 q ..) and one MFMA.
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int n = 0; n < G::NB; ++n) {
-        i32x8 vf;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2*)(Vc + vaddr[n] + (64 * hk + 16 * q) * G::RB));
-          vf[2 * q] = r2[0];
-          vf[2 * q + 1] = r2[1];
-        }
-        acc[n] = mfma8(vf, pf, acc[n]);
-      }
+      pv_mfmas(pf, Vc, hk);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4 * kAheadV8, 0);
 #pragma unroll
       for (int i = 0; i < G::NB; ++i) {
@@ -383,59 +402,15 @@ fwd_fp8_kernel(Params8 p) {
   // of the time (otherwise each block is products, softmax, products in sequence, and only the
   // other wave of the SIMD can fill the gaps).  Between the regions a vector read of the last
   // product issued (x += 0) waits until it has read its operands before the next region's LDS
-  // loads may reuse their registers (the FP8 MFMA operand hazard of the tile below).
+  // loads may reuse their registers (the FP8 MFMA operand hazard described in tile above).
   auto tile_fast = [&](const lds8_t* Kc, const lds8_t* Vc) __attribute__((always_inline)) {
-    constexpr int NS = 2 * G::KC;                     // score MFMAs of a 64-key block
     constexpr int kValuPerMfma = (120 + NS - 1) / NS;  // a block's softmax over its MFMAs
     const float bias = m_run - (float)kPScaleLog2;    // fixed and finite: p times 64
-    auto kfrag = [&](int hk, int bl, int c) __attribute__((always_inline)) {
-      const lds8_t* rb = Kc + (64 * hk + 32 * bl) * G::RB;
-      const u32x4 a0 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][0]);
-      const u32x4 a1 = *reinterpret_cast<const lds_u32x4*>(rb + kaddr[c][1]);
-      return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-    };
-    auto vfrag = [&](int hk, int n) __attribute__((always_inline)) {
-      i32x8 vf;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i32x2*)(Vc + vaddr[n] + (64 * hk + 16 * q) * G::RB));
-        vf[2 * q] = r2[0];
-        vf[2 * q + 1] = r2[1];
-      }
-      return vf;
-    };
-    auto score_mfmas = [&](f32x16 (&sc)[2], int hk) __attribute__((always_inline)) {
-#pragma unroll
-      for (int bl = 0; bl < 2; ++bl) {
-        sc[bl] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < G::KC; ++c) sc[bl] = mfma8(kfrag(hk, bl, c), qf[c], sc[bl]);
-      }
-    };
-    // Probabilities as e4m3 in k-slot order (the B operand of P V), their unrounded sum.
-    auto probs = [&](const f32x16 (&sc)[2], i32x8& pf) __attribute__((always_inline)) {
-      float rs = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        float e[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) e[t] = fast_exp2(fmaf(sc[w >> 2][4 * (w & 3) + t], sl2, -bias));
-        rs += (e[0] + e[1]) + (e[2] + e[3]);
-        pf[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
-      }
-      return rs;
-    };
-    auto pv_mfmas = [&](const i32x8& pf, int hk) __attribute__((always_inline)) {
-#pragma unroll
-      for (int n = 0; n < G::NB; ++n) acc[n] = mfma8(vfrag(hk, n), pf, acc[n]);
-    };
     f32x16 s0[2], s1[2];
     i32x8 pf0, pf1;
     // S(0): the score products of keys 0..63 (K reads kAhead8 MFMAs ahead).
     __builtin_amdgcn_sched_barrier(0);
-    score_mfmas(s0, 0);
+    score_mfmas(s0, Kc, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 2 * kAhead8, 0);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -446,8 +421,8 @@ fwd_fp8_kernel(Params8 p) {
     s0[1][15] += 0.f;
     __builtin_amdgcn_sched_barrier(0);
     // A: S(1) under the softmax of block 0.
-    score_mfmas(s1, 1);
-    float rs0 = probs(s0, pf0);
+    score_mfmas(s1, Kc, 1);
+    float rs0 = probs(s0, bias, pf0, std::false_type{});
     // The sums feed l only at the tile's end; without this use the adds (and the exponentials
     // they read) would be moved there, after every product of the tile.
     asm volatile("" : "+v"(rs0));
@@ -462,8 +437,8 @@ fwd_fp8_kernel(Params8 p) {
     s1[1][15] += 0.f;
     __builtin_amdgcn_sched_barrier(0);
     // B: P V of block 0 under the softmax of block 1.
-    pv_mfmas(pf0, 0);
-    float rs1 = probs(s1, pf1);
+    pv_mfmas(pf0, Vc, 0);
+    float rs1 = probs(s1, bias, pf1, std::false_type{});
     asm volatile("" : "+v"(rs1));
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4 * kAheadV8, 0);
 #pragma unroll
@@ -476,7 +451,7 @@ fwd_fp8_kernel(Params8 p) {
     acc[G::NB - 1][15] += 0.f;
     __builtin_amdgcn_sched_barrier(0);
     // C: P V of block 1.
-    pv_mfmas(pf1, 1);
+    pv_mfmas(pf1, Vc, 1);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead8, 4 * kAheadV8, 0);
 #pragma unroll
     for (int i = 0; i < G::NB; ++i) {
