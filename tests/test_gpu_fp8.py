@@ -145,6 +145,17 @@ def test_fp8_workload_16k_every_query_tile(name):
     _check_sampled(q8, k8, v8, scales, w["causal"], 1 / w["d"] ** 0.5, go, gl, 128, w["seed"])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_long_sequence_every_query_tile(causal):
+    # 65573 keys (a ragged last tile) in the eight-wave grid; a row of every 256-row query tile.
+    B, H, Hkv, N, d = 1, 2, 1, 65573, 128
+    say(f"fa_fwd_fp8 N={N} causal={causal}, a row of every 256-row query tile of every head")
+    q8, k8, v8, scales, _ = fp8_inputs(B, H, Hkv, N, d, seed=431)
+    go, gl = _run(q8, k8, v8, scales, causal)
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    _check_sampled(q8, k8, v8, scales, causal, 1 / d ** 0.5, go, gl, 256, 431)
+
+
 # The first pass fixes each row's reference 2^4 above the maximum of its first 128 keys; a
 # probability above 7.25 (64 p > 464) has no e4m3 code, and the workgroup recomputes with the
 # lagging reference.  A key equal to a row's own query scores about |q|^2 / sqrt(d), far above

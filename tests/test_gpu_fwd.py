@@ -271,6 +271,17 @@ def test_prefill_16k_workload_every_query_tile(name):
     _check_every_tile(q, k, v, o.cpu(), lse.cpu(), w["causal"], None, 1 / 128 ** 0.5, 256, w["seed"])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_every_query_tile(causal):
+    # 65573 keys (1025 key tiles, a ragged last one): the eight-wave grid over long rows.
+    B, H, Hkv, N, d = 1, 2, 1, 65573, 128
+    say(f"fa_fwd N={N} causal={causal}: a row of every 256-row query tile of every head")
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=31)
+    o, lse = _run(q, k, v, causal)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    _check_every_tile(q, k, v, o.cpu(), lse.cpu(), causal, None, 1 / d ** 0.5, 256, 31)
+
+
 def test_gqa_varlen_workload_every_query_tile():
     w = WORKLOADS["gqa_varlen_8k"]
     say("fa_fwd GQA causal varlen B=4 H=32 Hkv=8 N=8192: a row of every 256-row tile of every head")
