@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward and the paged decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {fwd,fwd_causal,fwd_4k,fwd_gqa,fwd_fp8,bwd,prefill_paged,prefill_paged_short,decode,copy} [--steps K]
+    python bench.py --only {fwd,fwd_causal,fwd_4k,fwd_gqa,fwd_fp8,bwd,prefill_paged,prefill_paged_short,decode,copy,fwd_sweep} [--steps K]
 
 One step is one pass of the whole hot path over its synthetic batch:
   * fa_fwd on B=1 H=8 N=16384 d=128 bf16 Q/K/V, non-causal (the headline workload), then
@@ -376,6 +376,33 @@ def only(args, torch, dev, wf, wd):
           flush=True)
 
 
+def sweep(args, torch, dev):
+    """fa_fwd over sequence lengths, B=1 H=8 d=128 bf16, both masks: one JSON line per case
+    (kernel configuration as the launcher picks it), then the engine clock under the largest."""
+    from io_aware_attention_02_amd import accounting as acc
+    from io_aware_attention_02_amd import fa_fwd
+    from io_aware_attention_02_amd.inputs import prefill_inputs
+
+    B, H, d = 1, 8, 128
+    fn = None
+    for N in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+        q, k, v, _ = prefill_inputs(B, H, H, N, d, "bf16", seed=7)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        for causal in (False, True):
+            fn = lambda: fa_fwd(q, k, v, o, lse, causal=causal)  # noqa: E731
+            ms = _time_calls(torch, fn, args.steps, warmup=args.warmup, warm_s=0.3)
+            f = acc.attention_flops(B, H, N, d, causal=causal)
+            print(json.dumps({"only": "fwd_sweep", "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                              "ms_per_call": round(ms, 4), "TFLOP/s": round(f / ms / 1e9, 1),
+                              "frac": round(f / ms / 1e9 / acc.MI355X_BF16_DENSE_TFLOPS, 4)}),
+                  flush=True)
+    clock = clock_under_load(torch, fn)
+    print(json.dumps({"only": "fwd_sweep", "engine_clock": clock.report(
+        "over 2.5 s of the last case (N=65536, causal)")}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,7 +411,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--only", choices=["fwd", "fwd_causal", "fwd_4k", "fwd_gqa", "fwd_fp8", "bwd",
-                                       "prefill_paged", "prefill_paged_short", "decode", "copy"],
+                                       "prefill_paged", "prefill_paged_short", "decode", "copy",
+                                       "fwd_sweep"],
                     default=None,
                     help="time one kernel alone (profiler runs); prints a short JSON line")
     args = ap.parse_args()
@@ -403,6 +431,9 @@ def main():
     dev = torch.device("cuda:0")
     wf = WORKLOADS["prefill_16k"]
     wd = WORKLOADS["paged_decode"]
+    if args.only == "fwd_sweep":
+        sweep(args, torch, dev)
+        return
     if args.only is not None:
         only(args, torch, dev, wf, wd)
         return
