@@ -71,8 +71,7 @@ struct Params {
 // The order changes no result.
 constexpr int kMaxRanked = 512;
 template <int NW>
-__device__ int by_work(const Params& p, int pos, int* buf) {
-  const int S = p.total / (p.H * p.n_qt);
+__device__ int by_work(const Params& p, int S, int pos, int* buf) {  // S: sequences in the grid
   if (S > kMaxRanked) return pos;
   int* w = buf;                   // key length of each sequence
   int* order = buf + kMaxRanked;  // sequence at each rank
@@ -94,7 +93,10 @@ __device__ int by_work(const Params& p, int pos, int* buf) {
 // buffers, and the two partial results (output, reference maximum, row sum) are combined
 // exactly at the end, as the online softmax combines any two blocks of keys
 // ("FlashAttention优化" §3.2.2).
-template <int D, bool CAUSAL, int NW, int NG = 1>
+// PAIR (causal grids that one round of 256-row tiles would leave to their heaviest tile): the
+// workgroup computes query tile i and then tile n_qt - 1 - i, so every workgroup has the same
+// number of key tiles to visit.
+template <int D, bool CAUSAL, int NW, int NG = 1, bool PAIR = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(Params p) {
   static_assert(NG == 1 || NG == 2, "one or two key groups");
@@ -128,20 +130,21 @@ fwd_bf16_kernel(Params p) {
   // divide evenly, XCD x takes units x, x+8, x+16, ... so every XCD holds the same mix of
   // sequences (causal work grows with the square of a sequence's length).
   const int lam = xcd_remap(blockIdx.x, p.total);
-  const int per_unit = p.group * p.n_qt;
+  const int n_slots = PAIR ? (p.n_qt + 1) / 2 : p.n_qt;  // query tiles (pairs) per head
+  const int per_unit = p.group * n_slots;
   const int units = p.total / per_unit;
   int unit = lam / per_unit;
   const int rem = lam - unit * per_unit;
   if (units % kXcds == 0) unit = (unit % (units / kXcds)) * kXcds + unit / (units / kXcds);
   int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
-  if (p.seq_lens != nullptr) b = by_work<NW>(p, b, rank_buf);  // heaviest first
+  if (p.seq_lens != nullptr) b = by_work<NW>(p, units / p.Hkv, b, rank_buf);  // heaviest first
   // Inside a unit the group's query heads take consecutive slots for each query tile: heads that
   // read the same K/V rows run side by side (shared L2 lines), and every head's heaviest tiles
   // come before any head's lighter ones.
   int qt = rem / p.group;
   const int hi = rem - qt * p.group;
-  if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
+  if (CAUSAL && !PAIR) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
   const int H = p.H, N = p.N;
   const int h = g * p.group + hi;
   const int bh = b * H + h;
@@ -149,13 +152,16 @@ fwd_bf16_kernel(Params p) {
   int L = N;
   if (p.seq_lens != nullptr) L = min(max(p.seq_lens[b], 0), N);
 
-  const int q0 = qt * kBM;
   const bf16* Qg = p.q + (size_t)bh * N * D;
   const bf16* Kg = p.k + (size_t)(b * p.Hkv + g) * N * D;
   const bf16* Vg = p.v + (size_t)(b * p.Hkv + g) * N * D;
   bf16* Og = p.o + (size_t)bh * N * D;
   float* LSEg = p.lse + (size_t)bh * N;
 
+  // One query tile: the whole computation of its rows (returns early for a tile of padding rows
+  // and, with two key groups, for group 1 once it has handed over its partial result).
+  auto work = [&](const int qt) __attribute__((always_inline)) {
+  const int q0 = qt * kBM;
   if (q0 >= L) {  // every row of this tile is padding: O = 0, LSE = -inf
     const int rows = min(kBM, N - q0);
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -361,6 +367,15 @@ fwd_bf16_kernel(Params p) {
     }
     if (hh == 0) LSEg[qrow] = valid ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
   }
+  };
+  work(qt);
+  if constexpr (PAIR) {
+    const int qt2 = p.n_qt - 1 - qt;
+    if (qt2 != qt) {
+      __syncthreads();  // group 0 has read group 1's partial result out of the tile buffers
+      work(qt2);
+    }
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -382,6 +397,18 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // at most as many workgroups as CUs (two waves per SIMD where four waves would leave one),
   // else four waves, two workgroups per CU.
   const long long wide = (long long)a.B * a.H * ((a.N + 8 * kWQ - 1) / (8 * kWQ));
+  const long long pairs = (long long)a.B * a.H * (((a.N + 4 * kWQ - 1) / (4 * kWQ) + 1) / 2);
+  if constexpr (CAUSAL) {
+    if (wide >= kCUs && wide < 2 * kCUs && pairs >= kCUs) {
+      // One or two rounds of 256-row causal tiles run at the pace of the heaviest: 128-row
+      // tiles in pairs (i, n - 1 - i) instead, two key groups of four waves each.
+      p.n_qt = (a.N + 4 * kWQ - 1) / (4 * kWQ);
+      p.total = (int)pairs;
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 8, 2, true>), dim3(p.total), dim3(64 * 8), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+  }
   if (wide >= kCUs) {
     p.n_qt = (a.N + 8 * kWQ - 1) / (8 * kWQ);
     p.total = a.B * a.H * p.n_qt;

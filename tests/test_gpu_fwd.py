@@ -271,6 +271,37 @@ def test_prefill_16k_workload_every_query_tile(name):
     _check_every_tile(q, k, v, o.cpu(), lse.cpu(), w["causal"], None, 1 / 128 ** 0.5, 256, w["seed"])
 
 
+# Causal grids that one or two rounds of 256-row tiles would leave to their heaviest tile run
+# 128-row tiles in pairs (i, n - 1 - i): N = 8192 (64 tiles per head), N = 8000 (63: the middle
+# tile alone), grouped heads with a ragged and a full length (padding tiles inside pairs), d = 64.
+PAIRED = [
+    # (B, H, Hkv, N, d, lengths)
+    (1, 8, 8, 8192, 128, None),
+    (1, 8, 8, 8000, 128, None),
+    (2, 8, 2, 4096, 128, [4096, 2500]),
+    (1, 8, 8, 8192, 64, None),
+]
+
+
+def _paired_launch(B, H, N):
+    # The launcher's rule (fa_fwd_bf16.hip): 256-row tiles would give one or two rounds over the
+    # 256 CUs, and the pairs of 128-row tiles still give every CU a workgroup.
+    wide = B * H * -(-N // 256)
+    pairs = B * H * ((-(-N // 128) + 1) // 2)
+    return 256 <= wide < 512 and pairs >= 256
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=[f"B{c[0]}H{c[1]}Hkv{c[2]}N{c[3]}d{c[4]}" for c in PAIRED])
+def test_causal_paired_query_tiles(case):
+    B, H, Hkv, N, d, lens = case
+    assert _paired_launch(B, H, N)
+    say(f"fa_fwd causal paired tiles {case}: a row of every 128-row query tile of every head")
+    q, k, v, _ = prefill_inputs(B, H, Hkv, N, d, "bf16", seed=41)
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32)
+    o, lse = _run(q, k, v, True, seq_lens=sl)
+    _check_every_tile(q, k, v, o.cpu(), lse.cpu(), True, sl, 1 / d ** 0.5, 128, 41)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_sequence_every_query_tile(causal):
     # 65573 keys (1025 key tiles, a ragged last one): the eight-wave grid over long rows.
