@@ -161,212 +161,214 @@ fwd_bf16_kernel(Params p) {
   // One query tile: the whole computation of its rows (returns early for a tile of padding rows
   // and, with two key groups, for group 1 once it has handed over its partial result).
   auto work = [&](const int qt) __attribute__((always_inline)) {
-  const int q0 = qt * kBM;
-  if (q0 >= L) {  // every row of this tile is padding: O = 0, LSE = -inf
-    const int rows = min(kBM, N - q0);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < rows * G::CPR; i += kThreads)
-      *reinterpret_cast<u32x4*>(Og + (size_t)q0 * D + i * 8) = zero;
-    for (int r = tid; r < rows; r += kThreads) LSEg[q0 + r] = kNegInf;
-    return;
-  }
-
-  const int kv_end = CAUSAL ? min(L, q0 + kBM) : L;   // keys this workgroup needs
-  const int n_kt = (kv_end + kBN - 1) / kBN;
-  const int qw0 = q0 + wq * kWQ;
-  const int qrow = qw0 + c32;
-  // Tiles this wave needs (fewer than n_kt on the causal diagonal).
-  const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
-  const float sl2 = p.sl2;
-  int koff[NI_W], voff[NI_W];
-  tile_offsets<D, NWG, false>(koff, wq, lane);
-  tile_offsets<D, NWG, true>(voff, wq, lane);
-  auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt) __attribute__((always_inline)) {
-    load_tile<D, NWG>(Kd + gofs, Kg, jt * kBN, L, koff, wq);
-    load_tile<D, NWG>(Vd + gofs, Vg, jt * kBN, L, voff, wq);
-  };
-
-  // Issue the first loads before anything else: K_0 and V_0.
-  if (NG == 1 || grp < n_kt) load_kv(K0, V0, grp);  // the group's first tile
-
-  // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel; zero for padding
-  // rows, so that whatever they hold (NaN included) cannot reach their zero output.
-  bf16x8 qf[G::KC];
-#pragma unroll
-  for (int c = 0; c < G::KC; ++c) {
-    qf[c] = qrow < L ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
-                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  }
-  FragAddr<D> fa = frag_addr<D>(lane);
-  if constexpr (NG > 1) {
-#pragma unroll
-    for (int c = 0; c < G::KC; ++c) fa.k[c] += gofs;
-#pragma unroll
-    for (int n = 0; n < G::NB; ++n) fa.v[n] += gofs;
-  }
-
-  f32x16 acc[G::NB];
-#pragma unroll
-  for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
-  float m_run = kNegInf;  // reference maximum (log2 units); -inf until a key is seen
-  float l_run = 0.f;      // this lane's share of the row sum (relative to m_run)
-
-  f32x16 sA[2];
-
-  // The K/V loop runs in one of two modes.
-  //  * FAST (first try): every row keeps the maximum of its first tile as a fixed reference, so
-  //    nothing accumulated is ever rescaled and later tiles need no maximum at all.  A tile in
-  //    which some lane's share of the row sum exceeds 2^kTau -- the only way one of its
-  //    probabilities can exceed 2^kTau -- raises a flag; otherwise every probability stays far
-  //    inside the bf16/fp32 range.
-  //  * SAFE: the running maximum with a rescale of O and l whenever it grows
-  //    ("FlashAttention优化" §3.2.1), taken only if some wave of the workgroup raised the flag.
-  // With a fixed reference the output and the row sum are the same sums the recurrence forms, so
-  // both modes give the exact softmax.
-  enum { FIRST = 0, FAST = 1, SAFE = 2 };
-  bool flagged = false;
-  auto tile = [&](const lds_t* Kc, const lds_t* Vc, int key0, auto masked, auto mode) __attribute__((always_inline)) {
-    constexpr bool M = decltype(masked)::value;
-    constexpr int MODE = decltype(mode)::value;
-    scores<D>(sA, Kc, fa, qf);
-    if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
-    if constexpr (MODE == FAST) {
-      // No tile maximum: every probability is at most the lane's share of the tile's row sum,
-      // so that sum exceeding 2^kTau is the test that some score outgrew the reference.
-      const float rs = softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
-      flagged |= rs > kMaxProb;
-      l_run += rs;
+    const int q0 = qt * kBM;
+    if (q0 >= L) {  // every row of this tile is padding: O = 0, LSE = -inf
+      const int rows = min(kBM, N - q0);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      for (int i = tid; i < rows * G::CPR; i += kThreads)
+        *reinterpret_cast<u32x4*>(Og + (size_t)q0 * D + i * 8) = zero;
+      for (int r = tid; r < rows; r += kThreads) LSEg[q0 + r] = kNegInf;
       return;
     }
-    const float mx = tile_max(sA);
-    const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
-    if constexpr (MODE == SAFE) {
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // -inf only before any visible key
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      l_run = fmaf(alpha, l_run, softmax_pv<D, M, true>(acc, Vc, fa, sA, sl2, m_use, alpha));
-    } else {
-      m_run = (mt == kNegInf) ? 0.f : mt;
-      l_run += softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
-    }
-  };
 
-  // Iteration j computes the group's tile j * NG + grp from buffers j % 2 while its next tile
-  // loads into the others.  The buffer is fixed per instantiation, so every LDS access refers to
-  // one known buffer and the compiler never waits for the loads in flight.  Tiles [0, n_main)
-  // need no mask for any wave of the workgroup; the remaining ones (the causal diagonal, the
-  // ragged end) are masked.  Iterations are counted for the whole workgroup (n_it, one barrier
-  // each) and per wave (n_iw, the iterations whose tile the wave needs).
-  const int n_main = CAUSAL ? min(q0, L) / kBN : L / kBN;
-  const int n_mi = n_main / NG;                  // iterations whose tiles all need no mask
-  const int n_it = (n_kt + NG - 1) / NG;
-  const int n_iw = (n_kw - grp + NG - 1) / NG;
-  auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(parity)::value;
-    lds_t* const Kc = ODD ? K1 : K0;
-    lds_t* const Vc = ODD ? V1 : V0;
-    lds_t* const Kn = ODD ? K0 : K1;
-    lds_t* const Vn = ODD ? V0 : V1;
-    if ((j + 1) * NG + grp < n_kt) load_kv(Kn, Vn, (j + 1) * NG + grp);
-    if (j < n_iw) tile(Kc, Vc, (j * NG + grp) * kBN, masked, mode);
-    wait_loads();
-    __syncthreads();
-  };
-  using even = std::false_type;
-  using odd = std::true_type;
-  using unmasked = std::false_type;
-  using masked = std::true_type;
-  auto run = [&](auto mode) __attribute__((always_inline)) {
-    constexpr int MODE = decltype(mode)::value;
-    using first_mode = std::integral_constant<int, MODE == SAFE ? SAFE : FIRST>;
-    // Tile 0 (K_0 and V_0 are loading or loaded): the FAST pass takes its references from it.
-    wait_loads();
-    __syncthreads();
-    if (0 < n_mi) iter(0, even{}, unmasked{}, first_mode{});
-    else iter(0, even{}, masked{}, first_mode{});
-    int j = 1;
-    for (; j + 1 < n_mi; j += 2) {
-      iter(j, odd{}, unmasked{}, mode);
-      iter(j + 1, even{}, unmasked{}, mode);
+    const int kv_end = CAUSAL ? min(L, q0 + kBM) : L;   // keys this workgroup needs
+    const int n_kt = (kv_end + kBN - 1) / kBN;
+    const int qw0 = q0 + wq * kWQ;
+    const int qrow = qw0 + c32;
+    // Tiles this wave needs (fewer than n_kt on the causal diagonal).
+    const int n_kw = CAUSAL ? min(n_kt, (min(L, qw0 + kWQ) + kBN - 1) / kBN) : n_kt;
+    const float sl2 = p.sl2;
+    int koff[NI_W], voff[NI_W];
+    tile_offsets<D, NWG, false>(koff, wq, lane);
+    tile_offsets<D, NWG, true>(voff, wq, lane);
+    auto load_kv = [&](lds_t* Kd, lds_t* Vd, int jt) __attribute__((always_inline)) {
+      load_tile<D, NWG>(Kd + gofs, Kg, jt * kBN, L, koff, wq);
+      load_tile<D, NWG>(Vd + gofs, Vg, jt * kBN, L, voff, wq);
+    };
+
+    // Issue the first loads before anything else: K_0 and V_0.
+    if (NG == 1 || grp < n_kt) load_kv(K0, V0, grp);  // the group's first tile
+
+    // Q^T fragments (B operand of S^T = K Q^T), resident for the whole kernel; zero for padding
+    // rows, so that whatever they hold (NaN included) cannot reach their zero output.
+    bf16x8 qf[G::KC];
+#pragma unroll
+    for (int c = 0; c < G::KC; ++c) {
+      qf[c] = qrow < L ? *reinterpret_cast<const bf16x8*>(Qg + (size_t)qrow * D + c * 16 + hh * 8)
+                        : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    if (j < n_mi) {
-      iter(j, odd{}, unmasked{}, mode);
-      ++j;
+    FragAddr<D> fa = frag_addr<D>(lane);
+    if constexpr (NG > 1) {
+#pragma unroll
+      for (int c = 0; c < G::KC; ++c) fa.k[c] += gofs;
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) fa.v[n] += gofs;
     }
-    for (; j < n_it; ++j) {
-      if (j & 1) iter(j, odd{}, masked{}, mode);
-      else iter(j, even{}, masked{}, mode);
-    }
-  };
-  run(std::integral_constant<int, FAST>{});
-  if (__syncthreads_or(flagged)) {  // some row's maximum outgrew its reference: exact fallback
+
+    f32x16 acc[G::NB];
 #pragma unroll
     for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
-    m_run = kNegInf;
-    l_run = 0.f;
-    if (NG == 1 || grp < n_kt) load_kv(K0, V0, grp);
-    run(std::integral_constant<int, SAFE>{});
-  }
+    float m_run = kNegInf;  // reference maximum (log2 units); -inf until a key is seen
+    float l_run = 0.f;      // this lane's share of the row sum (relative to m_run)
 
-  float lt = add_xor32(l_run);
-  if constexpr (NG > 1) {
-    // Combine the two key groups' partial results for the same rows: group 1 hands its output
-    // accumulator, reference maximum and row sum over LDS (the tile buffers, free now) to the
-    // wave of group 0 that owns the same rows, lane for lane (the accumulator layouts match).
-    // A group whose row sum is 0 saw no key of the row and drops out; group 0 always holds the
-    // row's first key.
-    constexpr int kAccB = 64 * G::NB * 16 * 4;  // accumulator bytes per wave
-    static_assert(NWG == 4 && 2 * kAccB == NG * G::TILE, "two waves' accumulators per buffer");
-    f32x4* const xa = reinterpret_cast<f32x4*>((wq < 2 ? k0s : k1s) + (wq & 1) * kAccB);
-    float* const xm = reinterpret_cast<float*>(v0s) + wq * 128;
-    __syncthreads();  // every wave is done with the tile buffers
-    if (grp == 1) {
+    f32x16 sA[2];
+
+    // The K/V loop runs in one of two modes.
+    //  * FAST (first try): every row keeps the maximum of its first tile as a fixed reference, so
+    //    nothing accumulated is ever rescaled and later tiles need no maximum at all.  A tile in
+    //    which some lane's share of the row sum exceeds 2^kTau -- the only way one of its
+    //    probabilities can exceed 2^kTau -- raises a flag; otherwise every probability stays far
+    //    inside the bf16/fp32 range.
+    //  * SAFE: the running maximum with a rescale of O and l whenever it grows
+    //    ("FlashAttention优化" §3.2.1), taken only if some wave of the workgroup raised the flag.
+    // With a fixed reference the output and the row sum are the same sums the recurrence forms, so
+    // both modes give the exact softmax.
+    enum { FIRST = 0, FAST = 1, SAFE = 2 };
+    bool flagged = false;
+    auto tile = [&](const lds_t* Kc, const lds_t* Vc, int key0, auto masked,
+                    auto mode) __attribute__((always_inline)) {
+      constexpr bool M = decltype(masked)::value;
+      constexpr int MODE = decltype(mode)::value;
+      scores<D>(sA, Kc, fa, qf);
+      if constexpr (M) mask_scores<CAUSAL>(sA, key0, L, qrow, hh);
+      if constexpr (MODE == FAST) {
+        // No tile maximum: every probability is at most the lane's share of the tile's row sum,
+        // so that sum exceeding 2^kTau is the test that some score outgrew the reference.
+        const float rs = softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
+        flagged |= rs > kMaxProb;
+        l_run += rs;
+        return;
+      }
+      const float mx = tile_max(sA);
+      const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
+      if constexpr (MODE == SAFE) {
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // -inf only before any visible key
+        const float alpha = fast_exp2(m_run - m_use);
+        m_run = m_new;
+        l_run = fmaf(alpha, l_run, softmax_pv<D, M, true>(acc, Vc, fa, sA, sl2, m_use, alpha));
+      } else {
+        m_run = (mt == kNegInf) ? 0.f : mt;
+        l_run += softmax_pv<D, M, false>(acc, Vc, fa, sA, sl2, m_run, 1.f);
+      }
+    };
+
+    // Iteration j computes the group's tile j * NG + grp from buffers j % 2 while its next tile
+    // loads into the others.  The buffer is fixed per instantiation, so every LDS access refers to
+    // one known buffer and the compiler never waits for the loads in flight.  Tiles [0, n_main)
+    // need no mask for any wave of the workgroup; the remaining ones (the causal diagonal, the
+    // ragged end) are masked.  Iterations are counted for the whole workgroup (n_it, one barrier
+    // each) and per wave (n_iw, the iterations whose tile the wave needs).
+    const int n_main = CAUSAL ? min(q0, L) / kBN : L / kBN;
+    const int n_mi = n_main / NG;                  // iterations whose tiles all need no mask
+    const int n_it = (n_kt + NG - 1) / NG;
+    const int n_iw = (n_kw - grp + NG - 1) / NG;
+    auto iter = [&](int j, auto parity, auto masked, auto mode) __attribute__((always_inline)) {
+      constexpr bool ODD = decltype(parity)::value;
+      lds_t* const Kc = ODD ? K1 : K0;
+      lds_t* const Vc = ODD ? V1 : V0;
+      lds_t* const Kn = ODD ? K0 : K1;
+      lds_t* const Vn = ODD ? V0 : V1;
+      if ((j + 1) * NG + grp < n_kt) load_kv(Kn, Vn, (j + 1) * NG + grp);
+      if (j < n_iw) tile(Kc, Vc, (j * NG + grp) * kBN, masked, mode);
+      wait_loads();
+      __syncthreads();
+    };
+    using even = std::false_type;
+    using odd = std::true_type;
+    using unmasked = std::false_type;
+    using masked = std::true_type;
+    auto run = [&](auto mode) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode)::value;
+      using first_mode = std::integral_constant<int, MODE == SAFE ? SAFE : FIRST>;
+      // Tile 0 (K_0 and V_0 are loading or loaded): the FAST pass takes its references from it.
+      wait_loads();
+      __syncthreads();
+      if (0 < n_mi) iter(0, even{}, unmasked{}, first_mode{});
+      else iter(0, even{}, masked{}, first_mode{});
+      int j = 1;
+      for (; j + 1 < n_mi; j += 2) {
+        iter(j, odd{}, unmasked{}, mode);
+        iter(j + 1, even{}, unmasked{}, mode);
+      }
+      if (j < n_mi) {
+        iter(j, odd{}, unmasked{}, mode);
+        ++j;
+      }
+      for (; j < n_it; ++j) {
+        if (j & 1) iter(j, odd{}, masked{}, mode);
+        else iter(j, even{}, masked{}, mode);
+      }
+    };
+    run(std::integral_constant<int, FAST>{});
+    if (__syncthreads_or(flagged)) {  // some row's maximum outgrew its reference: exact fallback
+#pragma unroll
+      for (int n = 0; n < G::NB; ++n) acc[n] = f32x16{};
+      m_run = kNegInf;
+      l_run = 0.f;
+      if (NG == 1 || grp < n_kt) load_kv(K0, V0, grp);
+      run(std::integral_constant<int, SAFE>{});
+    }
+
+    float lt = add_xor32(l_run);
+    if constexpr (NG > 1) {
+      // Combine the two key groups' partial results for the same rows: group 1 hands its output
+      // accumulator, reference maximum and row sum over LDS (the tile buffers, free now) to the
+      // wave of group 0 that owns the same rows, lane for lane (the accumulator layouts match).
+      // A group whose row sum is 0 saw no key of the row and drops out; group 0 always holds the
+      // row's first key.
+      constexpr int kAccB = 64 * G::NB * 16 * 4;  // accumulator bytes per wave
+      static_assert(NWG == 4 && 2 * kAccB == NG * G::TILE, "two waves' accumulators per buffer");
+      f32x4* const xa = reinterpret_cast<f32x4*>((wq < 2 ? k0s : k1s) + (wq & 1) * kAccB);
+      float* const xm = reinterpret_cast<float*>(v0s) + wq * 128;
+      __syncthreads();  // every wave is done with the tile buffers
+      if (grp == 1) {
+#pragma unroll
+        for (int n = 0; n < G::NB; ++n)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 v = {acc[n][4 * r4], acc[n][4 * r4 + 1], acc[n][4 * r4 + 2],
+                             acc[n][4 * r4 + 3]};
+            xa[(n * 4 + r4) * 64 + lane] = v;
+          }
+        xm[lane] = m_run;
+        xm[64 + lane] = lt;
+      }
+      __syncthreads();
+      if (grp == 1) return;
+      const float m1 = xm[lane], lt1 = xm[64 + lane];
+      const float m0 = lt > 0.f ? m_run : kNegInf;
+      const float mm = fmaxf(m0, lt1 > 0.f ? m1 : kNegInf);
+      const float a0 = lt > 0.f ? fast_exp2(m_run - mm) : 0.f;
+      const float a1 = lt1 > 0.f ? fast_exp2(m1 - mm) : 0.f;
 #pragma unroll
       for (int n = 0; n < G::NB; ++n)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 v = {acc[n][4 * r4], acc[n][4 * r4 + 1], acc[n][4 * r4 + 2], acc[n][4 * r4 + 3]};
-          xa[(n * 4 + r4) * 64 + lane] = v;
+          const f32x4 v = xa[(n * 4 + r4) * 64 + lane];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[n][4 * r4 + t] = acc[n][4 * r4 + t] * a0 + v[t] * a1;
         }
-      xm[lane] = m_run;
-      xm[64 + lane] = lt;
+      lt = lt * a0 + lt1 * a1;
+      m_run = mm;
     }
-    __syncthreads();
-    if (grp == 1) return;
-    const float m1 = xm[lane], lt1 = xm[64 + lane];
-    const float m0 = lt > 0.f ? m_run : kNegInf;
-    const float mm = fmaxf(m0, lt1 > 0.f ? m1 : kNegInf);
-    const float a0 = lt > 0.f ? fast_exp2(m_run - mm) : 0.f;
-    const float a1 = lt1 > 0.f ? fast_exp2(m1 - mm) : 0.f;
-#pragma unroll
-    for (int n = 0; n < G::NB; ++n)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 v = xa[(n * 4 + r4) * 64 + lane];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[n][4 * r4 + t] = acc[n][4 * r4 + t] * a0 + v[t] * a1;
-      }
-    lt = lt * a0 + lt1 * a1;
-    m_run = mm;
-  }
 
-  // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
-  if (qrow < N) {
-    const bool valid = qrow < L;
-    const float inv = valid ? 1.f / lt : 0.f;
+    // Epilogue: O = acc / l once; LSE = ln 2 * (m + log2 l).
+    if (qrow < N) {
+      const bool valid = qrow < L;
+      const float inv = valid ? 1.f / lt : 0.f;
 #pragma unroll
-    for (int n = 0; n < G::NB; ++n) {
+      for (int n = 0; n < G::NB; ++n) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[n][4 * r4 + 0] * inv, acc[n][4 * r4 + 1] * inv);
-        w[1] = pack_bf16x2(acc[n][4 * r4 + 2] * inv, acc[n][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(Og + (size_t)qrow * D + n * 32 + 8 * r4 + 4 * hh) = w;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[n][4 * r4 + 0] * inv, acc[n][4 * r4 + 1] * inv);
+          w[1] = pack_bf16x2(acc[n][4 * r4 + 2] * inv, acc[n][4 * r4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(Og + (size_t)qrow * D + n * 32 + 8 * r4 + 4 * hh) = w;
+        }
       }
+      if (hh == 0) LSEg[qrow] = valid ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
     }
-    if (hh == 0) LSEg[qrow] = valid ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
-  }
   };
   work(qt);
   if constexpr (PAIR) {
