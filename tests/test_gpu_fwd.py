@@ -223,6 +223,23 @@ def test_gqa_equals_repeated_kv_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_launch_shape_is_invisible(causal, d):
+    # The grid size picks the workgroup shape: 24 heads of 2048 rows run 128-row workgroups of
+    # four waves, 64 heads run 256-row workgroups of eight.  Both visit each row's keys in the
+    # same tiles and order, so the first 24 heads must come out bitwise the same either way: a
+    # head or a query tile mapped to the wrong data in one of the two launches shows up here.
+    say(f"fa_fwd 24 heads (four-wave) vs 64 heads (eight-wave), d={d}, causal={causal}")
+    N = 2048
+    q, k, v, _ = prefill_inputs(1, 64, 64, N, d, "bf16", seed=21)
+    o64, l64 = _run(q, k, v, causal)
+    o24, l24 = _run(q[:, :24].contiguous(), k[:, :24].contiguous(), v[:, :24].contiguous(), causal)
+    assert torch.equal(o24, o64[:, :24]) and torch.equal(l24, l64[:, :24])
+    _check(q[:, :2], k[:, :2], v[:, :2], o24[:, :2], l24[:, :2], causal, None, 1 / d ** 0.5,
+           TOL_O_BF16, rows=tile_rows(N, 128, head=0))
+
+
 def test_deterministic():
     say("fa_fwd determinism")
     q, k, v, _ = prefill_inputs(1, 4, 4, 2048, 128, "bf16", seed=11)
